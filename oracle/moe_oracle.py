@@ -1,0 +1,281 @@
+"""Plain, slow, fp64 CPU oracle of the routed-expert MoE forward over 4-bit codebook experts.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` may import or call this module. It shares no code with the GPU library
+(``codebook_quantized_moe_amd``) and imports nothing from it.
+
+Sources (the pages' titles; the section named on each function):
+
+* [card]  GLM-5.2-NF4-Lloyd-Experts-GPTQ model card (aidendle94): the storage format --
+  "Contents" (4-bit codes + E8M0 block scales, block 32 along K, low nibble = even K) and
+  "Codes are indices into the per-layer grid" (mag = code & 7, sign from bit 3,
+  w = sign * grid[mag] * 2^(scale_byte - 127); the grid is not amax-normalised) and
+  "What this is" (the E2M1 table {0, .5, 1, 1.5, 2, 3, 4, 6}).
+* [brief] "Round 7 -- Rewrite the GLM-5.2 routed-expert encoder" (CODEX_ROUND7.md of
+  GLM-5.2-EXL3-TR3v4-3.5bpw-MTP78): model geometry (256 routed experts, top-8, hidden 6144,
+  moe_intermediate 2048); decision 4 (I_e = silu(X Wg^T) * (X Wu^T)); decision 6 (down is
+  the [K=2048, N=6144] contraction of I_e); decision 7 (a consistent intermediate-channel
+  permutation of gate-N, up-N and down-K is exact because SwiGLU is elementwise).
+* [readme] README of GLM-5.2-EXL3-TR3v4-3.5bpw-MTP78, "What had to be fixed" / "Shared
+  residual rotations": expert outputs are router-weighted and summed back per token.
+
+Readings where the pages are silent (each is listed with its reason in the design notes):
+
+* gating: softmax over the k selected logits (textbook top-k gating);
+* top-k order: IEEE-754 totalOrder on the fp32 logit bits, descending, ties (identical
+  bits) to the lower expert id;
+* permutation: pairs p = t*k + j sorted by (expert, p), i.e. a stable sort; pairs whose id
+  is outside [0, E) are placed after all valid pairs, in p order;
+* dequant rounding: the exact product, rounded once to bf16 (round-to-nearest-even);
+  code 8 of a table whose entry 0 is 0 gives -0; scale byte 255 gives NaN (OCP MX E8M0);
+* the intermediate I is rounded to bf16 (the one stored activation inside the layer);
+  everything else accumulates in fp64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64", "rne_bf16", "total_order_key", "route_topk", "permute_by_expert",
+    "unpack_codes", "dequant_bf16", "layer_forward", "stack_forward", "E2M1_TABLE",
+]
+
+# [card] "What this is": the MXFP4 (E2M1) magnitudes, one per 3-bit magnitude index.
+E2M1_TABLE = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------------------------
+# bf16 helpers
+# ----------------------------------------------------------------------------------------------
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64 values (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def rne_bf16(x) -> np.ndarray:
+    """Round float64 values to bf16 (round to nearest, ties to even); returns uint16 bits.
+
+    Written from the bf16 format itself (1 sign bit, 8 exponent bits with bias 127,
+    7 stored significand bits; gradual underflow below 2^-126 in steps of 2^-133), one
+    rounding straight from fp64 (no detour through fp32, which would round twice for values
+    in bf16's subnormal range). NaN -> 0x7FC0 with the input's sign; overflow -> +-inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    sign = np.signbit(x).astype(np.uint32) << np.uint32(15)
+    a = np.abs(x)
+    out = np.zeros(a.shape, dtype=np.uint32)
+
+    nan = np.isnan(a)
+    inf = np.isinf(a)
+    fin = ~(nan | inf)
+
+    # normal range of the result: |x| >= 2^-126. |x| = m * 2^ex with m in [0.5, 1).
+    m, ex = np.frexp(np.where(fin, a, 1.0))
+    q = ex.astype(np.int64) - 1                      # |x| = (2m) * 2^q, 2m in [1, 2)
+    normal = fin & (a >= 2.0 ** -126)
+    # significand in units of the quantum 2^(q-7): in [128, 256); exact power-of-two scaling
+    sig = np.ldexp(np.where(normal, a, 0.0), np.where(normal, 7 - q, 0))
+    r = np.rint(sig)                                  # numpy rint: round half to even
+    carry = r >= 256.0
+    r = np.where(carry, 128.0, r)
+    q = np.where(carry, q + 1, q)
+    over = normal & (q > 127)
+    nbits = (((q + 127).astype(np.uint32) & np.uint32(0xFF)) << np.uint32(7)) | \
+        ((r.astype(np.int64) - 128).astype(np.uint32) & np.uint32(0x7F))
+    out = np.where(normal & ~over, nbits, out)
+    out = np.where(over | inf, np.uint32(0x7F80), out)
+
+    # subnormal range: multiples of 2^-133; a result of 128 units is the smallest normal.
+    sub = fin & (a < 2.0 ** -126)
+    units = np.rint(np.ldexp(np.where(sub, a, 0.0), 133))
+    out = np.where(sub, units.astype(np.uint32), out)
+
+    out = np.where(nan, np.uint32(0x7FC0), out)
+    return (out | sign).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------------------------
+# routing
+# ----------------------------------------------------------------------------------------------
+
+def total_order_key(logits) -> np.ndarray:
+    """uint32 keys whose unsigned order is IEEE-754 totalOrder of the fp32 values."""
+    b = np.ascontiguousarray(logits, dtype=np.float32).view(np.uint32)
+    neg = (b >> np.uint32(31)).astype(bool)
+    return np.where(neg, ~b, b | np.uint32(0x80000000)).astype(np.uint32)
+
+
+def route_topk(logits, k: int):
+    """Top-k experts per token and their gate values.
+
+    [brief] model geometry: each token selects 8 of 256 routed experts. Order of the k ids:
+    logit descending (totalOrder), ties to the lower expert id. Gate values: softmax over
+    the k selected logits, w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), in fp64.
+    Returns ids int32 [T, k], w float64 [T, k].
+    """
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    assert 1 <= k <= E
+    key = total_order_key(logits).astype(np.int64)
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    idx = np.arange(E)
+    for t in range(T):
+        order = np.lexsort((idx, -key[t]))  # primary: key descending; secondary: id ascending
+        sel = order[:k]
+        ids[t] = sel
+        lv = logits[t, sel].astype(np.float64)
+        ex = np.exp(lv - lv[0])
+        w[t] = ex / ex.sum()
+    return ids, w
+
+
+def permute_by_expert(ids, E: int):
+    """Group the T*k (token, slot) pairs by expert.
+
+    Pair p = t*k + j. Pairs are ordered by (expert id, p) ascending (a stable counting sort);
+    pairs whose id is outside [0, E) come last, in p order.
+    Returns offsets int32 [E+1] (offsets[e] = number of valid pairs with id < e; offsets[E]
+    = number of valid pairs), sorted_pair int32 [T*k] (sorted position -> p) and pair_pos
+    int32 [T*k] (p -> sorted position).
+    """
+    e = np.asarray(ids, dtype=np.int64).ravel()
+    P = e.size
+    p = np.arange(P)
+    valid = (e >= 0) & (e < E)
+    bucket = np.where(valid, e, E)
+    counts = np.bincount(bucket, minlength=E + 1)[:E]
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(counts)
+    sorted_pair = np.lexsort((p, bucket))
+    pair_pos = np.empty(P, np.int64)
+    pair_pos[sorted_pair] = p
+    return offsets.astype(np.int32), sorted_pair.astype(np.int32), pair_pos.astype(np.int32)
+
+
+# ----------------------------------------------------------------------------------------------
+# dequantisation
+# ----------------------------------------------------------------------------------------------
+
+def unpack_codes(codes) -> np.ndarray:
+    """[..., K/2] bytes -> [..., K] 4-bit codes; [card] "Contents": low nibble = even K."""
+    c = np.asarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape[:-1] + (c.shape[-1] * 2,), np.uint8)
+    out[..., 0::2] = c & 0x0F
+    out[..., 1::2] = c >> 4
+    return out
+
+
+def dequant_f64_exact(codes, scales, table) -> np.ndarray:
+    """The exact (unrounded) weight values of one matrix, in fp64.
+
+    [card] "Codes are indices into the per-layer grid": mag = code & 7 indexes the 8-entry
+    table, sign = -1 when bit 3 is set, w = sign * table[mag] * 2^(scale_byte - 127), one
+    scale byte per 32 consecutive K of a row. Scale byte 255 -> NaN (reading).
+    The product of an fp32 table entry and 2^(s - 127), s in [0, 254], is exact in fp64.
+    """
+    c = unpack_codes(codes)
+    s = np.repeat(np.asarray(scales, dtype=np.int64), 32, axis=-1)
+    assert s.shape == c.shape
+    tab = np.asarray(table, dtype=np.float32).astype(np.float64)
+    mag = tab[c & 7]
+    neg = (c & 8) != 0
+    v = np.ldexp(mag, s - 127)
+    v = np.where(neg, -v, v)                       # -0.0 for a zero magnitude
+    v = np.where(s == 255, np.where(neg, -np.nan, np.nan), v)
+    return v
+
+
+def dequant_bf16(codes, scales, table) -> np.ndarray:
+    """Dequantised weights as bf16 bit patterns (uint16): one RNE rounding of the exact value."""
+    return rne_bf16(dequant_f64_exact(codes, scales, table))
+
+
+def _expert_dense(codes, scales, table):
+    return bf16_to_f64(dequant_bf16(codes, scales, table))
+
+
+# ----------------------------------------------------------------------------------------------
+# the layer
+# ----------------------------------------------------------------------------------------------
+
+def _silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def layer_forward(x_bits, logits, k, lw, residual_bits=None, tokens=None, round_inter=True,
+                  routing=None):
+    """One routed-MoE layer forward in fp64.
+
+    x_bits: bf16 bits [T, H]; logits fp32 [T, E]; lw: an object with gate_codes,
+    gate_scales, up_codes, up_scales ([E, I, H/2], [E, I, H/32]), down_codes, down_scales
+    ([E, H, I/2], [E, H, I/32]), tables [n_tables, 8] fp32 and table_id [E].
+
+    Per pair p = (t, j) routed to expert e ([brief] decisions 4 and 6; [readme]):
+        g = Wg_e x_t,  u = Wu_e x_t                       (fp64 over bf16 values)
+        I_p = bf16(silu(g) * u)                           (round_inter)
+        z_p = Wd_e I_p                                    (fp64)
+        y_t = sum_j w[t, j] * z_(t, j)  (+ residual_t)
+    tokens: optional subset of token ids for which y is computed (routing is always done
+    for all tokens). routing: optional precomputed (ids, w) to use instead of route_topk.
+    Returns a dict with ids, w, offsets, sorted_pair, pair_pos, inter (bf16 bits
+    [T*k, I] by sorted position; rows of tokens outside ``tokens`` are zero) and y
+    (fp64 [T, H]; rows outside ``tokens`` are zero) and, with a residual, x_next bits.
+    """
+    x = bf16_to_f64(x_bits)
+    T, H = x.shape
+    E = lw.table_id.shape[0]
+    I = lw.gate_codes.shape[1]
+    if routing is None:
+        ids, w = route_topk(logits, k)
+    else:
+        ids, w = routing
+    offsets, sorted_pair, pair_pos = permute_by_expert(ids, E)
+    want = np.ones(T, bool) if tokens is None else np.isin(np.arange(T), tokens)
+    inter = np.zeros((T * k, I), np.uint16)
+    y = np.zeros((T, H), np.float64)
+    for e in range(E):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        if rows.size == 0:
+            continue
+        pairs = sorted_pair[rows]
+        tok = pairs // k
+        slot = pairs % k
+        keep = want[tok]
+        if not keep.any():
+            continue
+        rows, pairs, tok, slot = rows[keep], pairs[keep], tok[keep], slot[keep]
+        tab = lw.tables[int(lw.table_id[e])]
+        wg = _expert_dense(lw.gate_codes[e], lw.gate_scales[e], tab)
+        wu = _expert_dense(lw.up_codes[e], lw.up_scales[e], tab)
+        xs = x[tok]
+        g = xs @ wg.T
+        u = xs @ wu.T
+        del wg, wu
+        a = _silu(g) * u
+        if round_inter:
+            ib = rne_bf16(a)
+            inter[rows] = ib
+            a = bf16_to_f64(ib)
+        wd = _expert_dense(lw.down_codes[e], lw.down_scales[e], tab)
+        z = a @ wd.T
+        del wd
+        np.add.at(y, tok, w[tok, slot][:, None] * z)
+    out = dict(ids=ids, w=w, offsets=offsets, sorted_pair=sorted_pair, pair_pos=pair_pos,
+               inter=inter, y=y)
+    if residual_bits is not None:
+        out["x_next"] = rne_bf16(bf16_to_f64(residual_bits) + y)
+    return out
+
+
+def stack_forward(x_bits, layers, k):
+    """Free-running stack: X_{l+1} = bf16(X_l + y_l) (fp64 sum, one rounding).
+
+    layers: iterable of (logits, lw) per layer. Returns the final bf16 bits.
+    """
+    xb = np.asarray(x_bits, dtype=np.uint16)
+    for logits, lw in layers:
+        xb = layer_forward(xb, logits, k, lw, residual_bits=xb)["x_next"]
+    return xb

@@ -1,0 +1,312 @@
+"""Seeded synthetic inputs for the routed-expert MoE layer over 4-bit codebook experts.
+
+This package only produces inputs. It holds none of the forward pass: no decoding of codes,
+no contraction, no routing, no combine. The GPU library and the CPU oracle both consume
+its outputs and neither is imported by it.
+
+What it draws (the five workloads are described in ``CONFIGS``):
+
+* ``X``: bf16 activations from N(0, 1) (rounded to bf16 by torch's fp32 -> bf16 conversion).
+* router logits: fp32 N(0, 1), optionally with a Zipf(s) per-expert bias
+  ``b_e = -s * ln(rank_e)`` (rank a seeded permutation of 1..E), which makes a few experts
+  carry most of the routed mass.
+* a per-layer Lloyd-Max grid of 8 magnitudes fitted by plain Lloyd iterations on 1e5
+  half-normal samples (GLM-5.2-NF4-Lloyd-Experts-GPTQ model card, "What this is": the
+  grid is fitted by Lloyd-Max to Gaussian-like weight ratios; the pages fit a weighted
+  version over real weights, which are not available, so plain samples stand in).
+* expert weights N(0, 0.02), RTN-encoded to 4-bit sign+magnitude codes with E8M0
+  block-32 scales against the grid (or the E2M1 grid for selected experts), by the C
+  generator in ``csrc/``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsynth.so")
+
+# E2M1 magnitudes, one per 3-bit magnitude index (GLM-5.2-NF4-Lloyd-Experts-GPTQ model card,
+# "What this is": the MXFP4 grid {0, .5, 1, 1.5, 2, 3, 4, 6}).
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+
+# Experts that the model card's defect table lists as packed on the E2M1 grid
+# (GLM-5.2-NF4-Lloyd-Experts-GPTQ, "Known defect" table); the 8k prefill workload marks
+# these five expert ids as E2M1 experts.
+E2M1_DEFECT_EXPERTS = (164, 86, 15, 30, 139)
+
+WEIGHT_SIGMA = 0.02
+
+# seed streams
+S_X, S_LOGITS, S_ZIPF, S_LLOYD, S_WEIGHTS, S_PERM = 0, 1, 2, 3, 4, 5
+
+
+def build_lib(force: bool = False) -> str:
+    """Compile the C generator with gcc (a host build; no GPU code)."""
+    if os.path.exists(_LIB_PATH) and not force:
+        return _LIB_PATH
+    src = os.path.join(_HERE, "csrc")
+    objs = []
+    for name, extra in (("synth.c", []), ("synth_normal.c", ["-ffast-math"])):
+        obj = os.path.join(src, name.replace(".c", ".o"))
+        subprocess.check_call(["gcc", "-O3", "-march=x86-64-v3", "-fopenmp", "-fPIC", *extra,
+                               "-c", os.path.join(src, name), "-o", obj])
+        objs.append(obj)
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(["gcc", "-shared", "-fopenmp", *objs, "-o", tmp, "-lm", "-lmvec"])
+    os.replace(tmp, _LIB_PATH)
+    for o in objs:
+        os.remove(o)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build_lib()
+        L = ctypes.CDLL(_LIB_PATH)
+        i64, u64, dbl, vp = ctypes.c_int64, ctypes.c_uint64, ctypes.c_double, ctypes.c_void_p
+        L.synth_key.restype = u64
+        L.synth_key.argtypes = [i64] * 6
+        L.synth_normal_f32.restype = None
+        L.synth_normal_f32.argtypes = [u64, i64, i64, i64, dbl, vp, vp, vp]
+        L.synth_rtn_encode.restype = i64
+        L.synth_rtn_encode.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.synth_rtn_normal.restype = i64
+        L.synth_rtn_normal.argtypes = [u64, i64, i64, i64, dbl, vp, vp, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def key(*parts: int) -> int:
+    parts = tuple(int(p) for p in parts) + (0,) * (6 - len(parts))
+    return int(lib().synth_key(*parts))
+
+
+def rng(*parts: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(p) for p in parts])))
+
+
+# ----------------------------------------------------------------------------------------------
+# activations and router logits
+# ----------------------------------------------------------------------------------------------
+
+def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16) by torch's round-to-nearest-even conversion."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def make_x(cfg_id: int, T: int, H: int, layer: int = 0) -> np.ndarray:
+    """bf16 bits [T, H] from N(0, 1)."""
+    x = rng(cfg_id, S_X, layer).standard_normal((T, H), dtype=np.float32)
+    return bf16_bits_from_f32(x)
+
+
+def zipf_bias(cfg_id: int, E: int, s: float, layer: int = 0) -> np.ndarray:
+    """Per-expert fp32 bias -s*ln(rank_e), rank a seeded permutation of 1..E."""
+    ranks = rng(cfg_id, S_ZIPF, layer).permutation(E) + 1
+    return (-s * np.log(ranks.astype(np.float64))).astype(np.float32)
+
+
+def make_logits(cfg_id: int, T: int, E: int, layer: int = 0, zipf_s: float | None = None,
+                distinct: bool = True) -> np.ndarray:
+    """fp32 [T, E] router logits N(0, 1) (+ Zipf bias); rows redrawn until values are distinct."""
+    g = rng(cfg_id, S_LOGITS, layer)
+    z = g.standard_normal((T, E), dtype=np.float32)
+    if zipf_s is not None:
+        z = (z + zipf_bias(cfg_id, E, zipf_s, layer)[None, :]).astype(np.float32)
+    if distinct:
+        for t in range(T):
+            while len(np.unique(z[t])) != E:  # astronomically rare for continuous draws
+                row = g.standard_normal(E, dtype=np.float32)
+                if zipf_s is not None:
+                    row = row + zipf_bias(cfg_id, E, zipf_s, layer)
+                z[t] = row
+    return z
+
+
+# ----------------------------------------------------------------------------------------------
+# grids
+# ----------------------------------------------------------------------------------------------
+
+def lloyd_grid(cfg_id: int, layer: int = 0, n_samples: int = 100_000, tol: float = 1e-9,
+               max_iter: int = 500) -> np.ndarray:
+    """8 ascending fp32 magnitudes fitted by Lloyd iterations on |N(0,1)| samples.
+
+    Start at the sample quantiles (i + 1/2)/8; alternate nearest-level partition (cuts at the
+    midpoints) and centroid update, in fp64, until no level moves by more than ``tol``.
+    """
+    r = np.abs(rng(cfg_id, S_LLOYD, layer).standard_normal(n_samples))
+    r.sort()
+    levels = np.quantile(r, (np.arange(8) + 0.5) / 8.0)
+    for _ in range(max_iter):
+        cuts = 0.5 * (levels[1:] + levels[:-1])
+        idx = np.searchsorted(cuts, r, side="left")
+        new = levels.copy()
+        for i in range(8):
+            sel = r[idx == i]
+            if sel.size:
+                new[i] = sel.mean()
+        moved = np.max(np.abs(new - levels))
+        levels = new
+        if moved < tol:
+            break
+    return np.sort(levels).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------------------------
+# expert weights
+# ----------------------------------------------------------------------------------------------
+
+def rtn_encode(w: np.ndarray, grid: np.ndarray):
+    """RTN-encode an fp32 matrix [N, K]; returns (codes [N, K/2] u8, scales [N, K/32] u8)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    assert K % 32 == 0
+    codes = np.empty((N, K // 2), np.uint8)
+    scales = np.empty((N, K // 32), np.uint8)
+    grid = np.ascontiguousarray(grid, dtype=np.float32)
+    clamped = lib().synth_rtn_encode(_ptr(w), N, K, _ptr(grid), _ptr(codes), _ptr(scales))
+    assert clamped == 0, "block exponent outside the E8M0 range"
+    return codes, scales
+
+
+def normal_matrix(k: int, N: int, K: int, Kl: int | None = None, sigma: float = WEIGHT_SIGMA,
+                  row_src=None, col_src=None) -> np.ndarray:
+    out = np.empty((N, K), np.float32)
+    rs = None if row_src is None else np.ascontiguousarray(row_src, dtype=np.int32)
+    cs = None if col_src is None else np.ascontiguousarray(col_src, dtype=np.int32)
+    lib().synth_normal_f32(k, N, K, K if Kl is None else Kl, sigma, _ptr(rs), _ptr(cs), _ptr(out))
+    return out
+
+
+def rtn_normal_into(k: int, N: int, K: int, grid: np.ndarray, codes: np.ndarray,
+                    scales: np.ndarray, Kl: int | None = None, sigma: float = WEIGHT_SIGMA,
+                    row_src=None, col_src=None) -> None:
+    """Draw N(0, sigma) [N, K] and RTN-encode straight into the given (contiguous) arrays."""
+    assert codes.flags.c_contiguous and scales.flags.c_contiguous
+    assert codes.size == N * K // 2 and scales.size == N * K // 32
+    grid = np.ascontiguousarray(grid, dtype=np.float32)
+    rs = None if row_src is None else np.ascontiguousarray(row_src, dtype=np.int32)
+    cs = None if col_src is None else np.ascontiguousarray(col_src, dtype=np.int32)
+    clamped = lib().synth_rtn_normal(k, N, K, K if Kl is None else Kl, sigma, _ptr(rs), _ptr(cs),
+                                     _ptr(grid), _ptr(codes), _ptr(scales))
+    assert clamped == 0, "block exponent outside the E8M0 range"
+
+
+@dataclass
+class LayerWeights:
+    """One MoE layer's encoded experts. Codes [E, N, K/2], scales [E, N, K/32]."""
+    gate_codes: np.ndarray
+    gate_scales: np.ndarray
+    up_codes: np.ndarray
+    up_scales: np.ndarray
+    down_codes: np.ndarray
+    down_scales: np.ndarray
+    tables: np.ndarray          # [2, 8] fp32: 0 = layer Lloyd grid, 1 = E2M1
+    table_id: np.ndarray        # [E] uint8
+    perms: np.ndarray | None = None   # [E, I] int32: stored channel n holds logical channel perms[e, n]
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def nbytes(self) -> int:
+        return sum(a.nbytes for a in (self.gate_codes, self.gate_scales, self.up_codes,
+                                       self.up_scales, self.down_codes, self.down_scales))
+
+
+def make_layer(cfg_id: int, E: int, H: int, I: int, layer: int = 0, e2m1_experts=(),
+               permute: str | None = None, experts=None) -> LayerWeights:
+    """Encode a layer's experts.
+
+    permute: None, "random" (a random permutation of the I intermediate channels per expert)
+    or "block" (permutes whole 32-channel blocks and channels within each block). The stored
+    gate/up row n and the stored down column n hold logical channel perms[e, n]; the logical
+    (unpermuted) weights are the draws at the logical indices.
+    experts: optional subset of expert ids to encode (others left as zero bytes).
+    """
+    grid = lloyd_grid(cfg_id, layer)
+    tables = np.stack([grid, E2M1_GRID]).astype(np.float32)
+    table_id = np.zeros(E, np.uint8)
+    for e in e2m1_experts:
+        if e < E:
+            table_id[e] = 1
+    gate_codes = np.zeros((E, I, H // 2), np.uint8)
+    up_codes = np.zeros((E, I, H // 2), np.uint8)
+    down_codes = np.zeros((E, H, I // 2), np.uint8)
+    gate_scales = np.zeros((E, I, H // 32), np.uint8)
+    up_scales = np.zeros((E, I, H // 32), np.uint8)
+    down_scales = np.zeros((E, H, I // 32), np.uint8)
+    perms = None
+    if permute is not None:
+        perms = np.empty((E, I), np.int32)
+        for e in range(E):
+            g = rng(cfg_id, S_PERM, layer, e)
+            if permute == "random":
+                perms[e] = g.permutation(I)
+            elif permute == "block":
+                blocks = g.permutation(I // 32)
+                p = np.concatenate([b * 32 + g.permutation(32) for b in blocks])
+                perms[e] = p
+            else:
+                raise ValueError(permute)
+    ids = range(E) if experts is None else experts
+    for e in ids:
+        tab = tables[table_id[e]]
+        rs = None if perms is None else perms[e]
+        rtn_normal_into(key(cfg_id, S_WEIGHTS, layer, e, 0), I, H, tab, gate_codes[e],
+                        gate_scales[e], row_src=rs)
+        rtn_normal_into(key(cfg_id, S_WEIGHTS, layer, e, 1), I, H, tab, up_codes[e],
+                        up_scales[e], row_src=rs)
+        rtn_normal_into(key(cfg_id, S_WEIGHTS, layer, e, 2), H, I, tab, down_codes[e],
+                        down_scales[e], col_src=rs)
+    return LayerWeights(gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales,
+                        tables, table_id, perms,
+                        dict(cfg=cfg_id, layer=layer, E=E, H=H, I=I, permute=permute))
+
+
+# ----------------------------------------------------------------------------------------------
+# the five workloads
+# ----------------------------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Config:
+    cfg_id: int
+    name: str
+    H: int
+    I: int
+    E: int
+    k: int
+    T: int
+    layers: int = 1
+    zipf_s: float | None = None
+    e2m1: tuple = ()
+    permute: str | None = None
+    residual: bool = False
+
+
+CONFIGS = {
+    1: Config(1, "tiny", H=256, I=128, E=4, k=2, T=16),
+    2: Config(2, "glm_decode_t8", H=6144, I=2048, E=256, k=8, T=8),
+    3: Config(3, "glm_prefill_t2048_zipf", H=6144, I=2048, E=256, k=8, T=2048, zipf_s=1.0),
+    4: Config(4, "glm_stack32_decode_t64", H=6144, I=2048, E=256, k=8, T=64, layers=32,
+              residual=True),
+    5: Config(5, "glm_prefill_t8192_zipf_e2m1_perm", H=6144, I=2048, E=256, k=8, T=8192,
+              zipf_s=1.0, e2m1=E2M1_DEFECT_EXPERTS, permute="random"),
+}
+
+
+def expected_touched(E: int, k: int, T: int) -> float:
+    return E * (1.0 - (1.0 - k / E) ** T)

@@ -1,0 +1,354 @@
+"""Pins of the CPU oracle against facts fixed outside it: the pages' hand-worked decode
+values, closed forms of the bf16 format, library routines (torch's fp32->bf16 conversion,
+torch.topk, Python's sort, transformers' Mixtral experts and router) and algebraic
+invariants (consistent intermediate-channel permutation). CPU only."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f32_bits_to_bf16(v):
+    """bf16 bits of a value that is exactly representable in bf16 (the top half of fp32)."""
+    b = np.array(v, dtype=np.float32).view(np.uint32)
+    assert (b & 0xFFFF) == 0
+    return int(b >> 16)
+
+
+# ----------------------------------------------------------------------------------------------
+# bf16 rounding
+# ----------------------------------------------------------------------------------------------
+
+def test_rne_matches_torch_on_fp32_values():
+    g = np.random.default_rng(1)
+    # wide exponent range, both signs, fp32 subnormals, and values near the overflow edge
+    x = (g.standard_normal(200_000) * np.exp2(g.integers(-140, 127, 200_000))).astype(np.float32)
+    x = np.concatenate([x, np.array([0.0, -0.0, np.inf, -np.inf, 3.3895314e38, -3.3961e38,
+                                     1.1754942e-38, 1e-45, -1e-45], np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.rne_bf16(x.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_rne_single_rounding_closed_forms():
+    # 1 + 2^-8 is exactly halfway between 1 and 1 + 2^-7: ties to even -> 1.0
+    assert oracle.rne_bf16(np.array([1 + 2.0 ** -8]))[0] == 0x3F80
+    # 1 + 3*2^-8 is halfway between 1+2^-7 and 1+2^-6: ties to even -> 1 + 2^-6
+    assert oracle.rne_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 0x3F82
+    # just above the midpoint (not representable in fp32): rounds up; a detour through
+    # fp32 would land on the tie and round down to 1.0
+    assert oracle.rne_bf16(np.array([1 + 2.0 ** -8 + 2.0 ** -40]))[0] == 0x3F81
+    # bf16 subnormals are multiples of 2^-133
+    assert oracle.rne_bf16(np.array([2.0 ** -133]))[0] == 0x0001
+    assert oracle.rne_bf16(np.array([0.5 * 2.0 ** -133]))[0] == 0x0000      # tie -> even (0)
+    assert oracle.rne_bf16(np.array([1.5 * 2.0 ** -133]))[0] == 0x0002      # tie -> even (2)
+    assert oracle.rne_bf16(np.array([-127.5 * 2.0 ** -133]))[0] == 0x8080   # -> min normal
+    # largest finite bf16 is (2 - 2^-7) * 2^127; the midpoint to 2^128 rounds to inf
+    assert oracle.rne_bf16(np.array([(2 - 2.0 ** -7) * 2.0 ** 127]))[0] == 0x7F7F
+    assert oracle.rne_bf16(np.array([(2 - 2.0 ** -8) * 2.0 ** 127]))[0] == 0x7F80
+    assert oracle.rne_bf16(np.array([-0.0]))[0] == 0x8000
+    assert oracle.rne_bf16(np.array([np.nan]))[0] == 0x7FC0
+
+
+# ----------------------------------------------------------------------------------------------
+# decode: the pages' formula on hand-built bytes
+# ----------------------------------------------------------------------------------------------
+
+def _tables():
+    lloyd = np.array([0.2108, 0.4, 0.7, 0.95, 1.25, 1.6, 2.1, 2.75], np.float32)
+    return {"e2m1": oracle.E2M1_TABLE, "lloyd_m0": lloyd}
+
+
+def _read_golden():
+    rows = []
+    with open(os.path.join(GOLDEN, "decode_examples.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            tab, s, byte, ev, od = line.split()
+            rows.append((tab, int(s), int(byte, 16), ev, od))
+    return rows
+
+
+def _golden_bits(tok):
+    v = float(tok)
+    if tok.startswith("-") and v == 0.0:
+        return 0x8000
+    return _f32_bits_to_bf16(v)
+
+
+@pytest.mark.parametrize("row", _read_golden(), ids=lambda r: f"{r[0]}-s{r[1]}-{r[2]:#04x}")
+def test_decode_golden_bytes(row):
+    tab, s, byte, ev, od = row
+    table = _tables()[tab]
+    # one row of 32 codes (16 bytes), the example byte first, one scale byte
+    codes = np.zeros((1, 16), np.uint8)
+    codes[0, 0] = byte
+    scales = np.array([[s]], np.uint8)
+    bits = oracle.dequant_bf16(codes, scales, table)
+    assert bits.shape == (1, 32)
+    assert int(bits[0, 0]) == _golden_bits(ev), "even K (low nibble)"
+    assert int(bits[0, 1]) == _golden_bits(od), "odd K (high nibble)"
+
+
+def test_nibble_order_distinct_codes():
+    # byte j holds codes for K = 2j (low nibble) and 2j+1 (high nibble)
+    codes = np.array([[0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE] + [0] * 8], np.uint8)
+    c = oracle.unpack_codes(codes)[0]
+    np.testing.assert_array_equal(c[:16], np.arange(16))
+    v = oracle.bf16_to_f64(oracle.dequant_bf16(codes, np.array([[127]], np.uint8),
+                                               oracle.E2M1_TABLE))[0, :16]
+    expect = np.array([0, .5, 1, 1.5, 2, 3, 4, 6]) * 1.0
+    np.testing.assert_array_equal(v[:8], expect)
+    np.testing.assert_array_equal(v[8:], -expect)
+    assert np.signbit(v[8])
+
+
+def test_e2m1_zero_codes_every_scale():
+    s = np.arange(255, dtype=np.uint8)[:, None]                 # every scale byte but 255
+    codes = np.tile(np.array([[0x80] + [0] * 15], np.uint8), (255, 1))
+    bits = oracle.dequant_bf16(codes, s, oracle.E2M1_TABLE)
+    assert (bits[:, 0] == 0x0000).all()          # code 0 -> +0
+    assert (bits[:, 1] == 0x8000).all()          # code 8 -> -0
+    assert (bits[:, 2:] == 0x0000).all()
+
+
+def test_scale_byte_edges_closed_form():
+    t = oracle.E2M1_TABLE
+    def dq(byte, s):
+        codes = np.zeros((1, 16), np.uint8)
+        codes[0, 0] = byte
+        return oracle.dequant_bf16(codes, np.array([[s]], np.uint8), t)[0, :2]
+    # s = 0: 0.5 * 2^-127 = 2^-128 = 32 * 2^-133 -> subnormal bits 0x0020; 1.5*2^-127 -> 96
+    assert list(dq(0x31, 0)) == [0x0020, 0x0060]
+    # s = 254: low nibble 7: 6 * 2^127 overflows -> +inf; high nibble 1: 0.5 * 2^127 = 2^126
+    assert list(dq(0x17, 254)) == [0x7F80, 0x7E80]
+    # s = 255 -> NaN carrying the code's sign
+    assert list(dq(0x81, 255)) == [0x7FC0, 0xFFC0]
+    # a Lloyd magnitude with bits below bf16 precision, scaled into the subnormal range:
+    # (1 + 2^-8 + 2^-20) * 2^-127 = 64.25.. * 2^-133 -> 64 units
+    tab = np.array([1 + 2.0 ** -8 + 2.0 ** -20] * 8, np.float32)
+    codes = np.zeros((1, 16), np.uint8)
+    b = oracle.dequant_bf16(codes, np.array([[0]], np.uint8), tab)
+    assert b[0, 0] == 0x0040
+
+
+# ----------------------------------------------------------------------------------------------
+# routing and permutation
+# ----------------------------------------------------------------------------------------------
+
+def test_topk_matches_sort_and_torch_topk():
+    g = np.random.default_rng(2)
+    for (T, E, k) in [(16, 4, 2), (8, 256, 8), (33, 64, 64), (5, 17, 1)]:
+        logits = g.standard_normal((T, E)).astype(np.float32)
+        ids, w = oracle.route_topk(logits, k)
+        for t in range(T):
+            brute = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
+            assert list(ids[t]) == brute
+        tv, ti = torch.topk(torch.from_numpy(logits), k, dim=1, sorted=True)
+        np.testing.assert_array_equal(ids, ti.numpy())
+
+
+def test_topk_gate_weights_match_mixtral_router():
+    from transformers import MixtralConfig
+    from transformers.models.mixtral.modeling_mixtral import MixtralTopKRouter
+    g = np.random.default_rng(3)
+    T, E, k = 12, 256, 8
+    logits = g.standard_normal((T, E)).astype(np.float32)
+    ids, w = oracle.route_topk(logits, k)
+    cfg = MixtralConfig(hidden_size=E, num_local_experts=E, num_experts_per_tok=k)
+    r = MixtralTopKRouter(cfg).double()
+    with torch.no_grad():
+        r.weight.copy_(torch.eye(E, dtype=torch.float64))   # router logits = the given logits
+        # the router's softmax runs in fp32 (.float()); feed fp64 logits and compare at fp32
+        _, scores, idx = r(torch.from_numpy(logits.astype(np.float64)))
+    np.testing.assert_array_equal(ids, idx.numpy())
+    np.testing.assert_allclose(w, scores.double().numpy(), rtol=2e-6, atol=1e-7)
+    np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-14)
+
+
+def test_topk_ties_and_signed_zero():
+    logits = np.array([[1.0, 3.0, 3.0, -0.0, 0.0, 3.0]], np.float32)
+    ids, w = oracle.route_topk(logits, 5)
+    # equal values: lower id first; +0 ranks above -0 (IEEE totalOrder)
+    assert list(ids[0]) == [1, 2, 5, 0, 4]
+    np.testing.assert_allclose(w[0, :3], w[0, 0])
+
+
+def test_permute_is_stable_counting_sort():
+    g = np.random.default_rng(4)
+    for (T, k, E) in [(16, 2, 4), (8, 8, 256), (300, 8, 64), (1, 1, 1)]:
+        ids = g.integers(0, E, (T, k)).astype(np.int32)
+        off, sp, pp = oracle.permute_by_expert(ids, E)
+        flat = ids.ravel()
+        brute = sorted(range(T * k), key=lambda p: (flat[p], p))
+        assert list(sp) == brute
+        assert off[0] == 0 and off[E] == T * k
+        for e in range(E):
+            assert off[e + 1] - off[e] == (flat == e).sum()
+        np.testing.assert_array_equal(sp[pp], np.arange(T * k))
+
+
+def test_permute_invalid_ids_go_last():
+    ids = np.array([[3, -1], [0, 7], [2, 0]], np.int32)
+    off, sp, pp = oracle.permute_by_expert(ids, 4)
+    assert off[4] == 4                      # 4 valid pairs
+    assert list(sp) == [2, 5, 4, 0, 1, 3]   # e0: p2, p5; e2: p4; e3: p0; invalid: p1, p3
+
+
+# ----------------------------------------------------------------------------------------------
+# the layer: against transformers' Mixtral experts (an independent SwiGLU MoE implementation)
+# ----------------------------------------------------------------------------------------------
+
+def _mixtral_forward(x, ids, w, gate, up, down):
+    from transformers import MixtralConfig
+    from transformers.models.mixtral.modeling_mixtral import MixtralExperts
+    E, I, H = gate.shape
+    cfg = MixtralConfig(hidden_size=H, intermediate_size=I, num_local_experts=E,
+                        num_experts_per_tok=ids.shape[1], hidden_act="silu")
+    m = MixtralExperts(cfg).double()
+    with torch.no_grad():
+        m.gate_up_proj.copy_(torch.from_numpy(np.concatenate([gate, up], axis=1)))
+        m.down_proj.copy_(torch.from_numpy(down))
+        y = m(torch.from_numpy(x), torch.from_numpy(ids.astype(np.int64)), torch.from_numpy(w))
+    return y.numpy()
+
+
+def _dense(lw, perm_back=False):
+    E = lw.table_id.shape[0]
+    g, u, d = [], [], []
+    for e in range(E):
+        tab = lw.tables[lw.table_id[e]]
+        ge = oracle.bf16_to_f64(oracle.dequant_bf16(lw.gate_codes[e], lw.gate_scales[e], tab))
+        ue = oracle.bf16_to_f64(oracle.dequant_bf16(lw.up_codes[e], lw.up_scales[e], tab))
+        de = oracle.bf16_to_f64(oracle.dequant_bf16(lw.down_codes[e], lw.down_scales[e], tab))
+        if perm_back:   # stored channel n holds logical channel perms[e, n]
+            inv = np.argsort(lw.perms[e])
+            ge, ue, de = ge[inv], ue[inv], de[:, inv]
+        g.append(ge), u.append(ue), d.append(de)
+    return np.stack(g), np.stack(u), np.stack(d)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    c = synth.CONFIGS[1]
+    lw = synth.make_layer(1, c.E, c.H, c.I)
+    x = synth.make_x(1, c.T, c.H)
+    logits = synth.make_logits(1, c.T, c.E)
+    return c, lw, x, logits
+
+
+def test_layer_matches_mixtral_experts(tiny):
+    c, lw, x, logits = tiny
+    out = oracle.layer_forward(x, logits, c.k, lw, round_inter=False)
+    g, u, d = _dense(lw)
+    ref = _mixtral_forward(oracle.bf16_to_f64(x), out["ids"], out["w"], g, u, d)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_layer_all_experts_selected_matches_mixtral(tiny):
+    c, lw, x, logits = tiny
+    out = oracle.layer_forward(x, logits, c.E, lw, round_inter=False)     # k = E
+    g, u, d = _dense(lw)
+    ref = _mixtral_forward(oracle.bf16_to_f64(x), out["ids"], out["w"], g, u, d)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_layer_dense_bruteforce_scatter(tiny):
+    """Every expert on every token, gate values scattered into a zero [T, E] matrix."""
+    c, lw, x, logits = tiny
+    out = oracle.layer_forward(x, logits, c.k, lw, round_inter=False)
+    g, u, d = _dense(lw)
+    xf = torch.from_numpy(oracle.bf16_to_f64(x))
+    G = np.zeros((c.T, c.E))
+    for t in range(c.T):
+        G[t, out["ids"][t]] = out["w"][t]
+    y = torch.zeros(c.T, c.H, dtype=torch.float64)
+    for e in range(c.E):
+        h = torch.nn.functional.silu(xf @ torch.from_numpy(g[e]).T) * (xf @ torch.from_numpy(u[e]).T)
+        y += torch.from_numpy(G[:, e:e + 1]) * (h @ torch.from_numpy(d[e]).T)
+    np.testing.assert_allclose(out["y"], y.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_layer_intermediate_is_bf16_of_swiglu(tiny):
+    c, lw, x, logits = tiny
+    a = oracle.layer_forward(x, logits, c.k, lw, round_inter=True)
+    b = oracle.layer_forward(x, logits, c.k, lw, round_inter=False)
+    rel = np.linalg.norm(a["y"] - b["y"], axis=1) / np.linalg.norm(b["y"], axis=1)
+    assert rel.max() < 4e-3                     # bf16 rounding of I only
+    assert (a["inter"] != 0).any()
+
+
+def test_layer_tokens_subset_equals_full(tiny):
+    c, lw, x, logits = tiny
+    full = oracle.layer_forward(x, logits, c.k, lw)
+    sub = oracle.layer_forward(x, logits, c.k, lw, tokens=[3, 7])
+    np.testing.assert_array_equal(sub["y"][[3, 7]], full["y"][[3, 7]])
+
+
+# ----------------------------------------------------------------------------------------------
+# consistent intermediate-channel permutation ("Round 7" brief, decision 7)
+# ----------------------------------------------------------------------------------------------
+
+def _relayout_block_perm(lw, perms):
+    """Bytes of the same experts with intermediate channels permuted: stored channel n takes
+    logical channel perms[e, n]. perms must move whole 32-blocks / permute within blocks so the
+    down K-blocks (scales) stay whole. Works on unpacked codes (low nibble = even K)."""
+    import copy
+    q = copy.deepcopy(lw)
+    E = lw.table_id.shape[0]
+    for e in range(E):
+        p = perms[e]
+        q.gate_codes[e] = lw.gate_codes[e][p]
+        q.gate_scales[e] = lw.gate_scales[e][p]
+        q.up_codes[e] = lw.up_codes[e][p]
+        q.up_scales[e] = lw.up_scales[e][p]
+        c = oracle.unpack_codes(lw.down_codes[e])[:, p]
+        q.down_codes[e] = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+        q.down_scales[e] = lw.down_scales[e][:, p[::32] // 32]
+    return q
+
+
+def test_block_permutation_relayout_invariance(tiny):
+    c, lw, x, logits = tiny
+    g = np.random.default_rng(5)
+    perms = np.stack([np.concatenate([b * 32 + g.permutation(32) for b in g.permutation(c.I // 32)])
+                      for _ in range(c.E)])
+    q = _relayout_block_perm(lw, perms)
+    a = oracle.layer_forward(x, logits, c.k, lw)
+    b = oracle.layer_forward(x, logits, c.k, q)
+    np.testing.assert_allclose(b["y"], a["y"], rtol=1e-13, atol=1e-15)
+    # I is permuted per row: same multiset of values
+    np.testing.assert_array_equal(np.sort(a["inter"], 1), np.sort(b["inter"], 1))
+
+
+def test_random_permutation_baked_in_equals_unpermuted_dense():
+    """Weights drawn, permuted (stored channel n = logical perms[e, n]) and then encoded:
+    the routed forward on the stored bytes equals the dense forward on the un-permuted
+    dequantised weights (exact up to fp64 re-association)."""
+    E, H, I, k, T = 4, 256, 128, 2, 16
+    lw = synth.make_layer(1, E, H, I, permute="random", e2m1_experts=(2,))
+    x = synth.make_x(1, T, H)
+    logits = synth.make_logits(1, T, E)
+    out = oracle.layer_forward(x, logits, k, lw, round_inter=False)
+    g, u, d = _dense(lw, perm_back=True)
+    ref = _mixtral_forward(oracle.bf16_to_f64(x), out["ids"], out["w"], g, u, d)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-14)
+    assert (lw.perms[0] != np.arange(I)).any()
+
+
+def test_stack_residual_rounding(tiny):
+    c, lw, x, logits = tiny
+    one = oracle.layer_forward(x, logits, c.k, lw, residual_bits=x)
+    ref = oracle.rne_bf16(oracle.bf16_to_f64(x) + one["y"])
+    np.testing.assert_array_equal(one["x_next"], ref)
+    two = oracle.stack_forward(x, [(logits, lw), (logits, lw)], c.k)
+    step = oracle.layer_forward(one["x_next"], logits, c.k, lw, residual_bits=one["x_next"])
+    np.testing.assert_array_equal(two, step["x_next"])
