@@ -1,0 +1,221 @@
+// libmoeq C ABI: argument checks and dispatch. Every check runs before any launch, so a
+// failing call leaves the stream untouched. Declarations and the contract of each call are in
+// include/moeq.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "moeq.h"
+#include "moeq_kernels.h"
+
+using namespace moeq;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return MOEQ_OK;
+}
+
+int check_launch(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOEQ_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+int check_sizes(const char* what, int T, int k, int E) {
+    if (T < 0) return fail(MOEQ_EINVAL, "%s: T = %d must be >= 0", what, T);
+    if (E < 1 || E > MOEQ_MAX_EXPERTS)
+        return fail(MOEQ_EINVAL, "%s: E = %d must be in [1, %d]", what, E, MOEQ_MAX_EXPERTS);
+    if (k < 1 || k > E) return fail(MOEQ_EINVAL, "%s: k = %d must be in [1, E = %d]", what, k, E);
+    if ((long long)T * k >= (1LL << 31)) return fail(MOEQ_EINVAL, "%s: T*k too large", what);
+    return MOEQ_OK;
+}
+
+int check_tables(const char* what, const float* tables, int n_tables, TableArgs* ta) {
+    if (!tables) return fail(MOEQ_EINVAL, "%s: tables is NULL", what);
+    if (n_tables < 1 || n_tables > MOEQ_MAX_TABLES)
+        return fail(MOEQ_EINVAL, "%s: n_tables = %d must be in [1, %d]", what, n_tables, MOEQ_MAX_TABLES);
+    memset(ta, 0, sizeof(*ta));
+    ta->n = n_tables;
+    for (int t = 0; t < n_tables; ++t)
+        for (int m = 0; m < 8; ++m) {
+            const float v = tables[t * 8 + m];
+            if (!isfinite(v) || signbit(v))
+                return fail(MOEQ_EINVAL,
+                            "%s: tables[%d][%d] = %g: entries must be finite magnitudes with a clear sign bit",
+                            what, t, m, (double)v);
+            ta->v[t][m] = v;
+        }
+    return MOEQ_OK;
+}
+
+int check_hk(const char* what, int H, int I) {
+    if (H <= 0 || I <= 0) return fail(MOEQ_EINVAL, "%s: H = %d and I = %d must be positive", what, H, I);
+    if (H % 64 || I % 64)
+        return fail(MOEQ_EUNSUPPORTED, "%s: H = %d and I = %d must be multiples of 64", what, H, I);
+    return MOEQ_OK;
+}
+
+int persistent_blocks(long items) {
+    const long cap = (long)cu_count() * 8;
+    long b = (items + 3) / 4;
+    if (b > cap) b = cap;
+    return (int)(b < 1 ? 1 : b);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moeq_last_error(void) { return g_err; }
+
+size_t moeq_workspace_bytes(int T, int k, int E, int H, int I) {
+    (void)T; (void)k; (void)E; (void)H; (void)I;
+    return 0;
+}
+
+int moeq_route_topk(const float* logits, int T, int E, int k, int gating, int32_t* topk_ids,
+                    float* topk_w, void* stream) {
+    const char* w = "moeq_route_topk";
+    if (int r = check_sizes(w, T, k, E)) return r;
+    if (gating != MOEQ_GATING_SOFTMAX_TOPK) return fail(MOEQ_EINVAL, "%s: unknown gating %d", w, gating);
+    if (T == 0) return ok();
+    if (!logits || !topk_ids || !topk_w) return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    launch_route_topk(logits, T, E, k, topk_ids, topk_w, (hipStream_t)stream);
+    return check_launch(w);
+}
+
+int moeq_permute_by_expert(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_offsets,
+                           int32_t* sorted_pair, int32_t* pair_pos, void* stream) {
+    const char* w = "moeq_permute_by_expert";
+    if (int r = check_sizes(w, T, k, E)) return r;
+    if (!expert_offsets) return fail(MOEQ_EINVAL, "%s: expert_offsets is NULL", w);
+    if (T > 0 && (!topk_ids || !sorted_pair || !pair_pos)) return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    launch_permute(topk_ids, T * k, E, expert_offsets, sorted_pair, pair_pos, (hipStream_t)stream);
+    return check_launch(w);
+}
+
+static int projection(const char* w, bool gateup, const uint16_t* act, int T, int H, int I, int E,
+                      int k, const int32_t* offsets, const int32_t* sorted_pair, const float* topk_w,
+                      const uint8_t* codes0, const uint8_t* scales0, const uint8_t* codes1,
+                      const uint8_t* scales1, const float* tables, int n_tables,
+                      const uint8_t* table_id, void* out, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+    if (int r = check_sizes(w, T, k, E)) return r;
+    if (int r = check_hk(w, H, I)) return r;
+    SkinnyArgs a;
+    memset(&a, 0, sizeof(a));
+    if (int r = check_tables(w, tables, n_tables, &a.tables)) return r;
+    if (!act || !offsets || !sorted_pair || !codes0 || !scales0 || !table_id || !out ||
+        (gateup && (!codes1 || !scales1)) || (!gateup && !topk_w))
+        return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    if (!aligned(act, 16) || !aligned(codes0, 16) || !aligned(out, 16) || !aligned(scales0, 4) ||
+        (gateup && (!aligned(codes1, 16) || !aligned(scales1, 4))))
+        return fail(MOEQ_EUNSUPPORTED, "%s: codes, activations and outputs must be 16-byte aligned, scales 4-byte aligned", w);
+    const size_t need = moeq_workspace_bytes(T, k, E, H, I);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(MOEQ_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", w, need, ws_bytes);
+    if (T == 0) return ok();
+    a.act = act;
+    a.offsets = offsets;
+    a.sorted_pair = sorted_pair;
+    a.topk_w = topk_w;
+    a.codes0 = codes0;
+    a.scales0 = scales0;
+    a.codes1 = codes1;
+    a.scales1 = scales1;
+    a.table_id = table_id;
+    a.out = out;
+    a.T = T;
+    a.k = k;
+    a.E = E;
+    a.N = gateup ? I : H;
+    a.K = gateup ? H : I;
+    a.out_ld = gateup ? I : H;
+    const long touched = (long)(E < T * k ? E : T * k);
+    launch_skinny(a, gateup, persistent_blocks(touched * (a.N / 16)), stream);
+    return check_launch(w);
+}
+
+int moeq_gateup_swiglu(const uint16_t* x, int T, int H, int I, int E, int k,
+                       const int32_t* expert_offsets, const int32_t* sorted_pair,
+                       const uint8_t* gate_codes, const uint8_t* gate_scales,
+                       const uint8_t* up_codes, const uint8_t* up_scales, const float* tables,
+                       int n_tables, const uint8_t* table_id, uint16_t* inter, void* ws,
+                       size_t ws_bytes, void* stream) {
+    return projection("moeq_gateup_swiglu", true, x, T, H, I, E, k, expert_offsets, sorted_pair,
+                      nullptr, gate_codes, gate_scales, up_codes, up_scales, tables, n_tables,
+                      table_id, inter, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int moeq_down(const uint16_t* inter, int T, int H, int I, int E, int k,
+              const int32_t* expert_offsets, const int32_t* sorted_pair, const float* topk_w,
+              const uint8_t* down_codes, const uint8_t* down_scales, const float* tables,
+              int n_tables, const uint8_t* table_id, float* yp, void* ws, size_t ws_bytes,
+              void* stream) {
+    return projection("moeq_down", false, inter, T, H, I, E, k, expert_offsets, sorted_pair, topk_w,
+                      down_codes, down_scales, nullptr, nullptr, tables, n_tables, table_id, yp, ws,
+                      ws_bytes, (hipStream_t)stream);
+}
+
+int moeq_unpermute_combine(const float* yp, const int32_t* pair_pos, const int32_t* expert_offsets,
+                           int T, int k, int E, int H, const uint16_t* residual, uint16_t* y,
+                           void* stream) {
+    const char* w = "moeq_unpermute_combine";
+    if (int r = check_sizes(w, T, k, E)) return r;
+    if (H <= 0 || H % 4) return fail(MOEQ_EUNSUPPORTED, "%s: H = %d must be a positive multiple of 4", w, H);
+    if (T == 0) return ok();
+    if (!yp || !pair_pos || !expert_offsets || !y) return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    if (!aligned(yp, 16) || !aligned(y, 8) || (residual && !aligned(residual, 8)))
+        return fail(MOEQ_EUNSUPPORTED, "%s: yp must be 16-byte aligned, y and residual 8-byte aligned", w);
+    launch_combine(yp, pair_pos, expert_offsets, T, k, E, H, residual, y, (hipStream_t)stream);
+    return check_launch(w);
+}
+
+int moeq_debug_dequant(const uint8_t* codes, const uint8_t* scales, int E, int N, int K,
+                       const float* tables, int n_tables, const uint8_t* table_id, uint16_t* out,
+                       void* stream) {
+    const char* w = "moeq_debug_dequant";
+    if (E < 1 || N < 1 || K < 1) return fail(MOEQ_EINVAL, "%s: sizes must be positive", w);
+    if (K % 64) return fail(MOEQ_EUNSUPPORTED, "%s: K = %d must be a multiple of 64", w, K);
+    TableArgs ta;
+    if (int r = check_tables(w, tables, n_tables, &ta)) return r;
+    if (!codes || !scales || !table_id || !out) return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    if (!aligned(codes, 4) || !aligned(out, 16))
+        return fail(MOEQ_EUNSUPPORTED, "%s: codes must be 4-byte aligned, out 16-byte aligned", w);
+    const size_t total = (size_t)E * N * (K / 8);
+    size_t blocks = (total + 255) / 256;
+    if (blocks > (size_t)cu_count() * 16) blocks = (size_t)cu_count() * 16;
+    launch_dequant(codes, scales, E, N, K, table_id, ta, out, (int)blocks, (hipStream_t)stream);
+    return check_launch(w);
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Unpermute and combine: each token's k expert rows (gate weights already applied by the down
+// projection) are summed in fixed slot order in fp32, the optional residual is added, and the
+// row is rounded to bf16 (README of GLM-5.2-EXL3-TR3v4-3.5bpw-MTP78, "Shared residual
+// rotations": expert outputs are routing-weighted and summed back into the residual space).
+// One workgroup per (token, 1024-column chunk), flattened into one grid dimension; 16-byte loads of yp, 8-byte stores of y.
+#include "moeq_device.h"
+
+namespace moeq {
+
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ yp,
+                                                      const int32_t* __restrict__ pair_pos,
+                                                      const int32_t* __restrict__ offsets, int k,
+                                                      int E, int H,
+                                                      const uint16_t* residual, uint16_t* y) {
+    const int nchunk = (H / 4 + 255) / 256;
+    const int t = blockIdx.x / nchunk;
+    const int h = ((blockIdx.x % nchunk) * 256 + threadIdx.x) * 4;
+    if (h >= H) return;
+    const int valid = offsets[E];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    bool bad = false;
+    for (int j = 0; j < k; ++j) {
+        const int pos = pair_pos[(size_t)t * k + j];
+        if (pos >= valid) { bad = true; continue; }
+        const float4 v = *reinterpret_cast<const float4*>(yp + (size_t)pos * H + h);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if (residual) {
+        const uint2 r = *reinterpret_cast<const uint2*>(residual + (size_t)t * H + h);
+        acc.x += bf16_to_f32(r.x & 0xFFFFu); acc.y += bf16_to_f32(r.x >> 16);
+        acc.z += bf16_to_f32(r.y & 0xFFFFu); acc.w += bf16_to_f32(r.y >> 16);
+    }
+    if (bad) acc = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                               __builtin_nanf(""));
+    uint2 o;
+    o.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
+    o.y = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
+    *reinterpret_cast<uint2*>(y + (size_t)t * H + h) = o;
+}
+
+void launch_combine(const float* yp, const int32_t* pair_pos, const int32_t* offsets, int T, int k,
+                    int E, int H, const uint16_t* residual, uint16_t* y, hipStream_t stream) {
+    const int nchunk = (H / 4 + 255) / 256;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T * nchunk), dim3(256), 0, stream, yp, pair_pos, offsets, k, E, H,
+                       residual, y);
+}
+
+}  // namespace moeq

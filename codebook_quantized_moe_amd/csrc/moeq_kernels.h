@@ -1,0 +1,40 @@
+// Host-side launchers of the libmoeq kernels (defined in the .hip files next to this one).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moeq_device.h"
+
+namespace moeq {
+
+struct SkinnyArgs {
+    const uint16_t* act;          // gate|up: x [T, H] (natural); down: inter [T*k, I] (pair-split)
+    const int32_t* offsets;       // [E + 1]
+    const int32_t* sorted_pair;   // [T * k]
+    const float* topk_w;          // [T * k] (down only)
+    const uint8_t* codes0;        // gate or down codes [E, N, K/2]
+    const uint8_t* scales0;       // [E, N, K/32]
+    const uint8_t* codes1;        // up codes (gate|up only)
+    const uint8_t* scales1;
+    const uint8_t* table_id;      // [E]
+    void* out;                    // gate|up: inter bf16 [T*k, I]; down: yp fp32 [T*k, H]
+    int T, k, E;
+    int N;                        // weight rows per expert: I (gate|up) or H (down)
+    int K;                        // contraction length: H (gate|up) or I (down)
+    int out_ld;                   // row stride of out, in elements
+    TableArgs tables;
+};
+
+void launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                       hipStream_t stream);
+void launch_permute(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pair,
+                    int32_t* pair_pos, hipStream_t stream);
+void launch_skinny(const SkinnyArgs& a, bool gateup, int blocks, hipStream_t stream);
+void launch_combine(const float* yp, const int32_t* pair_pos, const int32_t* offsets, int T, int k,
+                    int E, int H, const uint16_t* residual, uint16_t* y, hipStream_t stream);
+void launch_dequant(const uint8_t* codes, const uint8_t* scales, int E, int N, int K,
+                    const uint8_t* table_id, const TableArgs& ta, uint16_t* out, int blocks,
+                    hipStream_t stream);
+
+}  // namespace moeq

@@ -1,0 +1,93 @@
+// Top-k routing: one wavefront per token ("Round 7" brief, Model geometry: top-8 of 256).
+//
+// Each lane holds up to 4 of the token's E <= 256 logits as 64-bit keys
+// (totalOrder(logit) << 32 | ~expert): the maximum key is the largest logit, and among equal
+// logits the lowest expert id. k rounds of a wave-wide max select the experts in order; the
+// gate values are a softmax over the k selected logits (fp32, fixed reduction order).
+#include "moeq_device.h"
+
+namespace moeq {
+
+__device__ __forceinline__ uint32_t total_order_key(float f) {
+    const uint32_t b = __float_as_uint(f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
+        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits, int T,
+                                                         int E, int k, int32_t* __restrict__ ids,
+                                                         float* __restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float* row = logits + (size_t)t * E;
+    uint64_t key[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        // padding entries: key 0 with an id above every real expert, never chosen first
+        key[j] = e < E ? ((uint64_t)total_order_key(row[e]) << 32) | (uint32_t)(~e)
+                       : (uint64_t)(uint32_t)(~(256 + e));
+    }
+    // slot r (0 <= r < k <= 256) is kept by lane r % 64 in its register r / 64
+    int my_id[4] = {0, 0, 0, 0};
+    float my_val[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < k; ++r) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int j = 1; j < 4; ++j) best = key[j] > best ? key[j] : best;
+        best = wave_max_u64(best);
+        const int win = (int)(~(uint32_t)best);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (key[j] == best) key[j] = 0;   // taken (keys are unique: ids differ)
+        if (lane == (r & 63)) {
+            const uint32_t kb = (uint32_t)(best >> 32);
+            const float v = __uint_as_float((kb & 0x80000000u) ? (kb & 0x7FFFFFFFu) : ~kb);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if ((r >> 6) == j) { my_id[j] = win; my_val[j] = v; }
+        }
+    }
+    const float l0 = __shfl(my_val[0], 0, 64);   // slot 0 holds the largest logit
+    float ex[4], part = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        ex[j] = (64 * j + lane < k) ? expf(my_val[j] - l0) : 0.0f;
+        part += ex[j];
+    }
+    const float sum = wave_sum_f32(part);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int slot = 64 * j + lane;
+        if (slot < k) {
+            ids[(size_t)t * k + slot] = my_id[j];
+            w[(size_t)t * k + slot] = ex[j] / sum;
+        }
+    }
+}
+
+void launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                       hipStream_t stream) {
+    const int blocks = (T + 3) / 4;
+    hipLaunchKernelGGL(route_topk_kernel, dim3(blocks), dim3(256), 0, stream, logits, T, E, k,
+                       ids, w);
+}
+
+}  // namespace moeq

@@ -1,0 +1,99 @@
+"""Buffers and call sequence of one routed-MoE layer forward over libmoeq's five calls.
+
+Plumbing only: torch allocates the device buffers once; ``forward`` enqueues
+route -> permute -> gate|up+SwiGLU -> down -> unpermute/combine on one stream with no
+host synchronisation in between.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import (moeq_down, moeq_gateup_swiglu, moeq_permute_by_expert, moeq_route_topk,
+               moeq_unpermute_combine, moeq_workspace_bytes)
+
+
+@dataclass
+class DeviceWeights:
+    """One layer's encoded experts on the device. Codes [E, N, K/2] u8, scales [E, N, K/32] u8."""
+    gate_codes: torch.Tensor
+    gate_scales: torch.Tensor
+    up_codes: torch.Tensor
+    up_scales: torch.Tensor
+    down_codes: torch.Tensor
+    down_scales: torch.Tensor
+    tables: np.ndarray          # host fp32 [n_tables, 8]
+    table_id: torch.Tensor      # device u8 [E]
+
+    @classmethod
+    def from_host(cls, lw, device="cuda"):
+        def d(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        return cls(d(lw.gate_codes), d(lw.gate_scales), d(lw.up_codes), d(lw.up_scales),
+                   d(lw.down_codes), d(lw.down_scales),
+                   np.ascontiguousarray(lw.tables, dtype=np.float32), d(lw.table_id))
+
+    @property
+    def E(self):
+        return self.gate_codes.shape[0]
+
+    @property
+    def I(self):
+        return self.gate_codes.shape[1]
+
+    @property
+    def H(self):
+        return self.gate_codes.shape[2] * 2
+
+
+class MoeLayer:
+    """Preallocated buffers for T tokens of a layer with E experts, top-k."""
+
+    def __init__(self, T: int, H: int, I: int, E: int, k: int, device="cuda"):
+        self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
+        P = T * k
+        i32 = dict(dtype=torch.int32, device=device)
+        self.topk_ids = torch.empty(P, **i32)
+        self.topk_w = torch.empty(P, dtype=torch.float32, device=device)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.sorted_pair = torch.empty(P, **i32)
+        self.pair_pos = torch.empty(P, **i32)
+        self.inter = torch.empty((P, I), dtype=torch.int16, device=device)
+        self.yp = torch.empty((P, H), dtype=torch.float32, device=device)
+        self.y = torch.empty((T, H), dtype=torch.int16, device=device)
+        self.ws_bytes = moeq_workspace_bytes(T, k, E, H, I)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
+
+    def route(self, logits, stream=None):
+        moeq_route_topk(logits, self.T, self.E, self.k, self.topk_ids, self.topk_w, stream=stream)
+
+    def permute(self, stream=None):
+        moeq_permute_by_expert(self.topk_ids, self.T, self.k, self.E, self.offsets,
+                               self.sorted_pair, self.pair_pos, stream=stream)
+
+    def gateup(self, x, w: DeviceWeights, stream=None):
+        moeq_gateup_swiglu(x, self.T, self.H, self.I, self.E, self.k, self.offsets,
+                           self.sorted_pair, w.gate_codes, w.gate_scales, w.up_codes,
+                           w.up_scales, w.tables, w.table_id, self.inter, self.ws, self.ws_bytes,
+                           stream=stream)
+
+    def down(self, w: DeviceWeights, stream=None):
+        moeq_down(self.inter, self.T, self.H, self.I, self.E, self.k, self.offsets,
+                  self.sorted_pair, self.topk_w, w.down_codes, w.down_scales, w.tables,
+                  w.table_id, self.yp, self.ws, self.ws_bytes, stream=stream)
+
+    def combine(self, residual=None, out=None, stream=None):
+        out = self.y if out is None else out
+        moeq_unpermute_combine(self.yp, self.pair_pos, self.offsets, self.T, self.k, self.E,
+                               self.H, residual, out, stream=stream)
+        return out
+
+    def forward(self, x, logits, w: DeviceWeights, residual=None, out=None, stream=None):
+        """x: int16 (bf16 bits) [T, H] cuda; logits fp32 [T, E] cuda. Returns y (bf16 bits)."""
+        self.route(logits, stream)
+        self.permute(stream)
+        self.gateup(x, w, stream)
+        self.down(w, stream)
+        return self.combine(residual, out, stream)

@@ -1,0 +1,186 @@
+/*
+ * moeq.h -- C ABI of libmoeq: the routed-expert MoE layer forward over 4-bit codebook
+ * experts, hand-written HIP for gfx950 (MI355X).
+ *
+ * What the layer computes (sources are the pages' titles and sections):
+ *   - geometry: "Round 7 -- Rewrite the GLM-5.2 routed-expert encoder", Ground truth /
+ *     Model geometry: 256 routed experts, top-8, hidden 6144, moe_intermediate 2048;
+ *   - expert: same brief, owner-locked decisions 4 and 6: I_e = silu(X Wg^T) * (X Wu^T),
+ *     then the down contraction I_e Wd^T (K = 2048, N = 6144);
+ *   - combine: README of GLM-5.2-EXL3-TR3v4-3.5bpw-MTP78, "What had to be fixed" and
+ *     "Shared residual rotations": expert outputs are router-weighted and summed per token;
+ *   - weights: GLM-5.2-NF4-Lloyd-Experts-GPTQ model card, "Contents" (4-bit codes, two per
+ *     byte with the even K index in the LOW nibble; one E8M0 scale byte per 32 consecutive K
+ *     of a row) and "Codes are indices into the per-layer grid" (w = (-1)^(code>>3) *
+ *     table[code & 7] * 2^(scale_byte - 127); the table is the layer's 8 fitted Lloyd-Max
+ *     magnitudes, or per expert the E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}).
+ *
+ * Shapes: T tokens, H hidden, I expert intermediate, E experts, k experts per token.
+ *   x        bf16 [T, H]                       (bf16 = uint16 bit patterns)
+ *   logits   fp32 [T, E]
+ *   gate/up  codes uint8 [E, I, H/2], scales uint8 [E, I, H/32]   (row n = output channel n)
+ *   down     codes uint8 [E, H, I/2], scales uint8 [E, H, I/32]
+ *   tables   fp32 [n_tables][8] HOST memory: 8 magnitudes per table
+ *   table_id uint8 [E] device: which table each expert decodes with
+ *
+ * Conventions shared by every call:
+ *   - All array pointers are DEVICE pointers owned by the caller, except `tables`, which is a
+ *     host pointer read during the call (its values are copied into the kernel arguments).
+ *   - The library never allocates, frees or synchronises. `stream` is a hipStream_t passed as
+ *     void* (NULL = the null stream); every call only enqueues work on it.
+ *   - Return value: MOEQ_OK, or a negative moeq_status; the arguments are checked before
+ *     anything is launched, and on error nothing is launched. moeq_last_error() gives a
+ *     thread-local message for the last failing call. Faults inside a kernel surface at the
+ *     caller's next synchronisation, as for any HIP launch.
+ *   - Results are deterministic: no floating-point atomics anywhere.
+ *   - Size limits: 1 <= k <= E <= 256; H and I multiples of 64; T*k < 2^31.
+ *   - Alignment: codes, x, inter and yp 16-byte aligned; scales 4-byte aligned.
+ */
+#ifndef MOEQ_H
+#define MOEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moeq_status {
+    MOEQ_OK = 0,
+    MOEQ_EINVAL = -1,        /* invalid argument (null pointer, bad size, bad table value) */
+    MOEQ_EUNSUPPORTED = -2,  /* valid but unsupported shape, alignment or mode */
+    MOEQ_EWORKSPACE = -3,    /* workspace missing or too small */
+    MOEQ_ELAUNCH = -4        /* a HIP launch reported an error */
+};
+
+/* Gate scoring. Only softmax over the k selected logits is defined: the pages say expert
+ * outputs are router-weighted but not how the weights are formed; this is textbook top-k
+ * gating (softmax of the kept logits). */
+enum moeq_gating { MOEQ_GATING_SOFTMAX_TOPK = 0 };
+
+#define MOEQ_MAX_EXPERTS 256
+#define MOEQ_MAX_TABLES 4
+
+/* Position of intermediate channel c inside a row of `inter` (see moeq_gateup_swiglu):
+ * within each aligned group of 8 channels the order is 0, 2, 4, 6, 1, 3, 5, 7. */
+static inline int moeq_inter_slot(int c) {
+    return (c & ~7) | (((c & 1) << 2) | ((c & 7) >> 1));
+}
+
+/* Thread-local message describing the last failing call of this thread ("" if none). */
+const char* moeq_last_error(void);
+
+/* Bytes of device workspace that moeq_gateup_swiglu and moeq_down need for these sizes
+ * (0 means they accept ws = NULL). */
+size_t moeq_workspace_bytes(int T, int k, int E, int H, int I);
+
+/*
+ * Top-k routing. For each token t, topk_ids[t, 0..k) are the k experts with the largest
+ * logits, in descending logit order under IEEE-754 totalOrder of the fp32 bit patterns;
+ * equal bit patterns go to the lower expert id. topk_w[t, j] = softmax over the k selected
+ * logits (fp32), w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0). The gate values are finite
+ * when the selected logits are. (Source for top-8 of 256: "Round 7" brief, Model geometry.)
+ *   logits   fp32 [T, E]   in
+ *   topk_ids int32 [T, k]  out
+ *   topk_w   fp32 [T, k]   out
+ * T = 0 is a no-op. Errors: MOEQ_EINVAL for null pointers, k < 1, k > E, E > 256, unknown
+ * gating.
+ */
+int moeq_route_topk(const float* logits, int T, int E, int k, int gating, int32_t* topk_ids,
+                    float* topk_w, void* stream);
+
+/*
+ * Group the T*k (token, slot) pairs by expert. Pair p = t*k + j with expert topk_ids[p].
+ * Pairs are ordered by (expert, p) ascending -- a stable counting sort built from an expert
+ * histogram and a wavefront prefix scan -- so the result is unique and deterministic.
+ *   topk_ids       int32 [T*k]  in
+ *   expert_offsets int32 [E+1]  out: rows of expert e are sorted positions
+ *                               [expert_offsets[e], expert_offsets[e+1]); expert_offsets[E]
+ *                               is the number of VALID pairs
+ *   sorted_pair    int32 [T*k]  out: sorted position -> pair p
+ *   pair_pos       int32 [T*k]  out: pair p -> sorted position
+ * A pair whose id lies outside [0, E) is not dropped silently: it is placed after every valid
+ * pair (positions >= expert_offsets[E], in p order), no expert computes it, and
+ * moeq_unpermute_combine writes NaN for its token. Callers detect it as expert_offsets[E] <
+ * T*k. Errors: MOEQ_EINVAL for null pointers or sizes out of range.
+ */
+int moeq_permute_by_expert(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_offsets,
+                           int32_t* sorted_pair, int32_t* pair_pos, void* stream);
+
+/*
+ * Fused gate|up projection and SwiGLU ("Round 7" brief, decision 4), with the weights decoded
+ * from 4-bit codes as they are streamed (model card, "Codes are indices into the per-layer
+ * grid"). For each sorted row r of expert e (pair p = sorted_pair[r], token t = p / k):
+ *     g = X[t] . Wg[e][n],  u = X[t] . Wu[e][n]          (fp32 accumulation)
+ *     inter[r][moeq_inter_slot(n)] = bf16(silu(g) * u)   (round to nearest even)
+ * Each weight is decoded exactly: bf16(sign * table[table_id[e]][code & 7] * 2^(s - 127)),
+ * one round-to-nearest-even of the exact product (s = 255 decodes to NaN).
+ *   x        bf16 [T, H]
+ *   expert_offsets, sorted_pair: from moeq_permute_by_expert
+ *   gate/up codes uint8 [E, I, H/2], scales uint8 [E, I, H/32]
+ *   tables   HOST fp32 [n_tables][8], 1 <= n_tables <= MOEQ_MAX_TABLES; every entry must be
+ *            finite and non-negative with a clear sign bit (they are magnitudes)
+ *   table_id uint8 [E]; an expert whose id is >= n_tables writes NaN rows (never a guess)
+ *   inter    bf16 [T*k, I] out, rows by sorted position, channels in moeq_inter_slot order;
+ *            only rows < expert_offsets[E] are written. It is the library's layout for the
+ *            intermediate, read back by moeq_down.
+ *   ws       device workspace of at least moeq_workspace_bytes(T, k, E, H, I) bytes
+ * Errors: MOEQ_EINVAL (null pointer, sizes, table values), MOEQ_EUNSUPPORTED (H or I not a
+ * multiple of 64, misalignment), MOEQ_EWORKSPACE.
+ */
+int moeq_gateup_swiglu(const uint16_t* x, int T, int H, int I, int E, int k,
+                       const int32_t* expert_offsets, const int32_t* sorted_pair,
+                       const uint8_t* gate_codes, const uint8_t* gate_scales,
+                       const uint8_t* up_codes, const uint8_t* up_scales, const float* tables,
+                       int n_tables, const uint8_t* table_id, uint16_t* inter, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * Down projection with the gate weight applied ("Round 7" brief, decision 6; README of
+ * GLM-5.2-EXL3-TR3v4-3.5bpw-MTP78, "What had to be fixed": router weighting happens in the
+ * down epilogue). For each sorted row r of expert e, pair p = sorted_pair[r]:
+ *     yp[r][h] = topk_w[p] * (inter[r] . Wd[e][h])       (fp32 accumulation)
+ *   inter  bf16 [T*k, I] from moeq_gateup_swiglu
+ *   topk_w fp32 [T*k] from moeq_route_topk
+ *   down codes uint8 [E, H, I/2], scales uint8 [E, H, I/32]
+ *   yp     fp32 [T*k, H] out; rows >= expert_offsets[E] are not written
+ * Tables, table_id, ws and errors as for moeq_gateup_swiglu.
+ */
+int moeq_down(const uint16_t* inter, int T, int H, int I, int E, int k,
+              const int32_t* expert_offsets, const int32_t* sorted_pair, const float* topk_w,
+              const uint8_t* down_codes, const uint8_t* down_scales, const float* tables,
+              int n_tables, const uint8_t* table_id, float* yp, void* ws, size_t ws_bytes,
+              void* stream);
+
+/*
+ * Sum each token's k expert rows back into the residual space (README of
+ * GLM-5.2-EXL3-TR3v4-3.5bpw-MTP78, "Shared residual rotations": routing-weighted and summed
+ * back). In fp32, slots in fixed order j = 0..k-1:
+ *     y[t] = bf16( sum_j yp[pair_pos[t*k + j]]  (+ residual[t]) )
+ *   yp        fp32 [T*k, H] from moeq_down (gate weights already applied)
+ *   pair_pos, expert_offsets: from moeq_permute_by_expert (a pair at a position >=
+ *             expert_offsets[E] had an invalid expert id: its token's row becomes NaN)
+ *   residual  bf16 [T, H] or NULL
+ *   y         bf16 [T, H] out; may be the same buffer as residual (in-place update)
+ * Errors: MOEQ_EINVAL for null pointers or bad sizes.
+ */
+int moeq_unpermute_combine(const float* yp, const int32_t* pair_pos, const int32_t* expert_offsets,
+                           int T, int k, int E, int H, const uint16_t* residual, uint16_t* y,
+                           void* stream);
+
+/*
+ * Test entry point: decode whole matrices with the same device decode path the two
+ * projections use (model card, "Codes are indices into the per-layer grid").
+ *   codes uint8 [E, N, K/2], scales uint8 [E, N, K/32], out bf16 [E, N, K] (natural K order)
+ * K must be a multiple of 64. Tables and table_id as above.
+ */
+int moeq_debug_dequant(const uint8_t* codes, const uint8_t* scales, int E, int N, int K,
+                       const float* tables, int n_tables, const uint8_t* table_id, uint16_t* out,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEQ_H */

@@ -1,0 +1,122 @@
+"""The C-ABI library loads, exports every symbol include/moeq.h declares, and rejects bad
+arguments before launching anything (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import codebook_quantized_moe_amd as mq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moeq.h")
+
+GOOD_TABLES = np.array([[0.13, 0.39, 0.66, 0.94, 1.26, 1.62, 2.07, 2.73],
+                        [0, .5, 1, 1.5, 2, 3, 4, 6]], np.float32)
+FAKE = 4096   # a non-null, 16-byte aligned address; never dereferenced by a failing call
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = set(re.findall(r"\b(moeq_[a-z_]+)\s*\(", src))
+    names.discard("moeq_inter_slot")           # static inline helper in the header
+    return sorted(names)
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert set(names) == set(mq.EXPORTED)
+    lib = ctypes.CDLL(mq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_inter_slot_matches_header_rule():
+    c = np.arange(64)
+    s = mq.inter_slot(c)
+    assert sorted(s) == list(range(64))
+    np.testing.assert_array_equal(s[:8], [0, 4, 1, 5, 2, 6, 3, 7])
+
+
+def _status(fn, *args, **kw):
+    with pytest.raises(mq.MoeqError) as ei:
+        fn(*args, **kw)
+    return ei.value.status
+
+
+def test_route_validation():
+    assert _status(mq.moeq_route_topk, FAKE, 4, 256, 0, FAKE, FAKE, stream=0) == mq.MOEQ_EINVAL
+    assert _status(mq.moeq_route_topk, FAKE, 4, 8, 9, FAKE, FAKE, stream=0) == mq.MOEQ_EINVAL
+    assert _status(mq.moeq_route_topk, FAKE, 4, 300, 8, FAKE, FAKE, stream=0) == mq.MOEQ_EINVAL
+    assert _status(mq.moeq_route_topk, None, 4, 256, 8, FAKE, FAKE, stream=0) == mq.MOEQ_EINVAL
+    assert _status(mq.moeq_route_topk, FAKE, 4, 256, 8, FAKE, FAKE, gating=3,
+                   stream=0) == mq.MOEQ_EINVAL
+    assert "gating" in mq.moeq_last_error()
+    mq.moeq_route_topk(None, 0, 256, 8, None, None, stream=0)       # T = 0: no-op, OK
+
+
+def test_permute_validation():
+    assert _status(mq.moeq_permute_by_expert, FAKE, 4, 8, 0, FAKE, FAKE, FAKE,
+                   stream=0) == mq.MOEQ_EINVAL
+    assert _status(mq.moeq_permute_by_expert, None, 4, 8, 256, FAKE, FAKE, FAKE,
+                   stream=0) == mq.MOEQ_EINVAL
+    assert _status(mq.moeq_permute_by_expert, FAKE, 4, 8, 256, None, FAKE, FAKE,
+                   stream=0) == mq.MOEQ_EINVAL
+    assert _status(mq.moeq_permute_by_expert, FAKE, 1 << 29, 8, 256, FAKE, FAKE, FAKE,
+                   stream=0) == mq.MOEQ_EINVAL
+
+
+def _gateup(**over):
+    a = dict(x=FAKE, T=8, H=6144, I=2048, E=256, k=8, expert_offsets=FAKE, sorted_pair=FAKE,
+             gate_codes=FAKE, gate_scales=FAKE, up_codes=FAKE, up_scales=FAKE,
+             tables=GOOD_TABLES, table_id=FAKE, inter=FAKE, ws=None, ws_bytes=0, stream=0)
+    a.update(over)
+    return a
+
+
+def test_gateup_validation():
+    bad = [
+        (dict(H=6000), mq.MOEQ_EUNSUPPORTED),
+        (dict(I=100), mq.MOEQ_EUNSUPPORTED),
+        (dict(k=0), mq.MOEQ_EINVAL),
+        (dict(E=257), mq.MOEQ_EINVAL),
+        (dict(x=None), mq.MOEQ_EINVAL),
+        (dict(table_id=None), mq.MOEQ_EINVAL),
+        (dict(gate_codes=FAKE + 8), mq.MOEQ_EUNSUPPORTED),
+        (dict(gate_scales=FAKE + 2), mq.MOEQ_EUNSUPPORTED),
+        (dict(tables=np.zeros((5, 8), np.float32)), mq.MOEQ_EINVAL),
+        (dict(tables=np.array([[np.nan] * 8], np.float32)), mq.MOEQ_EINVAL),
+        (dict(tables=np.array([[np.inf] + [1] * 7], np.float32)), mq.MOEQ_EINVAL),
+        (dict(tables=np.array([[-0.0] + [1] * 7], np.float32)), mq.MOEQ_EINVAL),
+        (dict(tables=np.array([[1.0] * 7 + [-2.0]], np.float32)), mq.MOEQ_EINVAL),
+    ]
+    for over, code in bad:
+        assert _status(mq.moeq_gateup_swiglu, **_gateup(**over)) == code, over
+
+
+def test_down_and_combine_validation():
+    assert _status(mq.moeq_down, FAKE, 8, 6144, 2048, 256, 8, FAKE, FAKE, None, FAKE, FAKE,
+                   GOOD_TABLES, FAKE, FAKE, stream=0) == mq.MOEQ_EINVAL       # topk_w NULL
+    assert _status(mq.moeq_down, FAKE, 8, 6144, 2048, 256, 8, FAKE, FAKE, FAKE, FAKE, FAKE,
+                   GOOD_TABLES, FAKE, FAKE + 4, stream=0) == mq.MOEQ_EUNSUPPORTED
+    assert _status(mq.moeq_unpermute_combine, FAKE, FAKE, FAKE, 8, 8, 256, 6146, None, FAKE,
+                   stream=0) == mq.MOEQ_EUNSUPPORTED
+    assert _status(mq.moeq_unpermute_combine, None, FAKE, FAKE, 8, 8, 256, 6144, None, FAKE,
+                   stream=0) == mq.MOEQ_EINVAL
+    assert _status(mq.moeq_unpermute_combine, FAKE, FAKE, FAKE, 8, 8, 256, 6144, FAKE + 2, FAKE,
+                   stream=0) == mq.MOEQ_EUNSUPPORTED
+
+
+def test_debug_dequant_validation():
+    assert _status(mq.moeq_debug_dequant, FAKE, FAKE, 1, 1, 96, GOOD_TABLES, FAKE, FAKE,
+                   stream=0) == mq.MOEQ_EUNSUPPORTED
+    assert _status(mq.moeq_debug_dequant, FAKE, FAKE, 0, 1, 64, GOOD_TABLES, FAKE, FAKE,
+                   stream=0) == mq.MOEQ_EINVAL
+
+
+def test_last_error_is_cleared_on_success():
+    _status(mq.moeq_route_topk, None, 4, 256, 8, FAKE, FAKE, stream=0)
+    assert mq.moeq_last_error() != ""
+    mq.moeq_route_topk(None, 0, 256, 8, None, None, stream=0)
+    assert mq.moeq_last_error() == ""

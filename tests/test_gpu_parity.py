@@ -1,0 +1,289 @@
+"""GPU parity of libmoeq against the fp64 CPU oracle, through the C ABI.
+
+Bars: routing ids, the permutation and every dequantised weight bit-exact; gate values to
+fp32 rounding; the intermediate to bf16 rounding; layer outputs within 5e-3 row-relative
+(||y_gpu - y_ref|| / ||y_ref|| per token row, y_ref in fp64 over the same bf16 weights and
+activations)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+ROW_REL_TOL = 5e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import codebook_quantized_moe_amd  # noqa: F401  (fails loudly when not built)
+
+
+def _mq():
+    import codebook_quantized_moe_amd as mq
+    return mq
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def u16(t):
+    return host(t).view(np.uint16)
+
+
+def row_rel(y_gpu_bits, y_ref):
+    g = oracle.bf16_to_f64(y_gpu_bits)
+    num = np.linalg.norm(g - y_ref, axis=1)
+    den = np.linalg.norm(y_ref, axis=1)
+    return num / np.maximum(den, 1e-300)
+
+
+def run_layer(lw, x_bits, logits, k, residual=False):
+    mq = _mq()
+    T, H = x_bits.shape
+    E, I = lw.table_id.shape[0], lw.gate_codes.shape[1]
+    w = mq.DeviceWeights.from_host(lw)
+    L = mq.MoeLayer(T, H, I, E, k)
+    x = dev(x_bits.view(np.int16))
+    y = L.forward(x, dev(logits), w, residual=x if residual else None)
+    torch.cuda.synchronize()
+    return dict(ids=host(L.topk_ids).reshape(T, k), w=host(L.topk_w).reshape(T, k),
+                offsets=host(L.offsets), sorted_pair=host(L.sorted_pair),
+                pair_pos=host(L.pair_pos), inter=u16(L.inter), y=u16(y))
+
+
+def unslot(inter, I):
+    return inter[:, _mq().inter_slot(np.arange(I))]
+
+
+def check_layer(out, ref, k, tokens=None, inter_rows=True):
+    np.testing.assert_array_equal(out["ids"], ref["ids"])
+    np.testing.assert_allclose(out["w"], ref["w"], rtol=2e-6, atol=1e-7)
+    np.testing.assert_array_equal(out["offsets"], ref["offsets"])
+    np.testing.assert_array_equal(out["sorted_pair"], ref["sorted_pair"])
+    np.testing.assert_array_equal(out["pair_pos"], ref["pair_pos"])
+    T = out["y"].shape[0]
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    if inter_rows:
+        I = ref["inter"].shape[1]
+        rows = ref["pair_pos"].reshape(T, k)[toks].ravel()
+        gi = oracle.bf16_to_f64(unslot(out["inter"], I)[rows])
+        ri = oracle.bf16_to_f64(ref["inter"][rows])
+        rel_i = np.linalg.norm(gi - ri, axis=1) / np.linalg.norm(ri, axis=1)
+        assert rel_i.max() < ROW_REL_TOL, rel_i.max()
+    rel = row_rel(out["y"][toks], ref["y"][toks])
+    assert np.all(np.isfinite(rel)) and rel.max() <= ROW_REL_TOL, rel.max()
+    return rel.max()
+
+
+# ----------------------------------------------------------------------------------------------
+# dequant: bit-exact for every scale byte and every code, several tables
+# ----------------------------------------------------------------------------------------------
+
+def test_debug_dequant_bitexact_all_bytes_and_scales():
+    mq = _mq()
+    E, N, K = 3, 256, 128
+    g = np.random.default_rng(11)
+    codes = g.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    codes[:, :, :16] = np.arange(256, dtype=np.uint8).reshape(16, 16)[np.arange(N) % 16]
+    scales = np.empty((E, N, K // 32), np.uint8)
+    scales[:] = (np.arange(N)[:, None] + np.arange(K // 32)[None, :] * 64) % 256
+    odd = np.array([0.0, 1e-40, 2.0 ** -126, 1 + 2.0 ** -8 + 2.0 ** -20, 1 + 3 * 2.0 ** -8,
+                    3.0e38, 1.99609375, 0.2108], np.float32)
+    tables = np.stack([synth.lloyd_grid(1, 0), synth.E2M1_GRID, odd]).astype(np.float32)
+    table_id = np.array([0, 1, 2], np.uint8)
+    out = torch.empty((E, N, K), dtype=torch.int16, device="cuda")
+    mq.moeq_debug_dequant(dev(codes), dev(scales), E, N, K, tables, dev(table_id), out)
+    got = u16(out)
+    for e in range(E):
+        ref = oracle.dequant_bf16(codes[e], scales[e], tables[table_id[e]])
+        mism = np.argwhere(got[e] != ref)
+        assert mism.size == 0, (e, mism[:5], got[e][tuple(mism[0])], ref[tuple(mism[0])])
+
+
+def test_debug_dequant_invalid_table_id_is_nan():
+    mq = _mq()
+    E, N, K = 2, 16, 64
+    codes = np.full((E, N, K // 2), 0x31, np.uint8)
+    scales = np.full((E, N, K // 32), 127, np.uint8)
+    tables = np.stack([synth.E2M1_GRID]).astype(np.float32)
+    out = torch.empty((E, N, K), dtype=torch.int16, device="cuda")
+    mq.moeq_debug_dequant(dev(codes), dev(scales), E, N, K, tables,
+                          dev(np.array([0, 1], np.uint8)), out)
+    v = oracle.bf16_to_f64(u16(out))
+    assert np.all(v[0, :, 0::2] == 0.5) and np.all(v[0, :, 1::2] == 1.5)
+    assert np.all(np.isnan(v[1]))
+
+
+# ----------------------------------------------------------------------------------------------
+# routing and permutation: bit-exact
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k,zipf", [(16, 4, 2, None), (8, 256, 8, None), (2048, 256, 8, 1.0),
+                                        (33, 64, 64, None), (1, 17, 1, None), (5, 256, 256, None)])
+def test_route_topk_bitexact(T, E, k, zipf):
+    mq = _mq()
+    logits = synth.make_logits(7, T, E, zipf_s=zipf)
+    ids = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    mq.moeq_route_topk(dev(logits), T, E, k, ids, w)
+    rid, rw = oracle.route_topk(logits, k)
+    np.testing.assert_array_equal(host(ids).reshape(T, k), rid)
+    np.testing.assert_allclose(host(w).reshape(T, k), rw, rtol=2e-6, atol=1e-7)
+
+
+def test_route_ties_and_signed_zero():
+    mq = _mq()
+    logits = np.array([[1.0, 3.0, 3.0, -0.0, 0.0, 3.0] + [-5.0] * 58,
+                       [np.float32(-np.inf)] * 60 + [2.0, 2.0, -1.0, 2.0]], np.float32)
+    T, E, k = 2, 64, 5
+    ids = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    mq.moeq_route_topk(dev(logits), T, E, k, ids, w)
+    rid, _ = oracle.route_topk(logits, k)
+    np.testing.assert_array_equal(host(ids).reshape(T, k), rid)
+
+
+@pytest.mark.parametrize("T,k,E", [(16, 2, 4), (8, 8, 256), (2048, 8, 256), (8192, 8, 256),
+                                   (1, 1, 1), (129, 3, 7)])
+def test_permute_bitexact(T, k, E):
+    mq = _mq()
+    ids = np.random.default_rng(T * 31 + E).integers(0, E, T * k).astype(np.int32)
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    mq.moeq_permute_by_expert(dev(ids), T, k, E, off, sp, pp)
+    ro, rs, rp = oracle.permute_by_expert(ids.reshape(T, k), E)
+    np.testing.assert_array_equal(host(off), ro)
+    np.testing.assert_array_equal(host(sp), rs)
+    np.testing.assert_array_equal(host(pp), rp)
+
+
+def test_permute_invalid_ids_are_placed_last():
+    mq = _mq()
+    ids = np.array([3, -1, 0, 7, 2, 0, 4, 1000], np.int32)
+    E = 4
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(8, dtype=torch.int32, device="cuda")
+    pp = torch.empty(8, dtype=torch.int32, device="cuda")
+    mq.moeq_permute_by_expert(dev(ids), 4, 2, E, off, sp, pp)
+    ro, rs, rp = oracle.permute_by_expert(ids.reshape(4, 2), E)
+    np.testing.assert_array_equal(host(off), ro)
+    np.testing.assert_array_equal(host(sp), rs)
+    np.testing.assert_array_equal(host(pp), rp)
+    assert host(off)[E] == 4
+
+
+# ----------------------------------------------------------------------------------------------
+# whole layer
+# ----------------------------------------------------------------------------------------------
+
+def _case(cfg_id, T, E, H, I, k, **kw):
+    lw = synth.make_layer(cfg_id, E, H, I, **kw)
+    x = synth.make_x(cfg_id, T, H)
+    logits = synth.make_logits(cfg_id, T, E)
+    return lw, x, logits
+
+
+def test_layer_tiny_config():
+    c = synth.CONFIGS[1]
+    lw, x, logits = _case(1, c.T, c.E, c.H, c.I, c.k)
+    out = run_layer(lw, x, logits, c.k)
+    ref = oracle.layer_forward(x, logits, c.k, lw)
+    check_layer(out, ref, c.k)
+
+
+@pytest.mark.parametrize("T,E,H,I,k", [(37, 8, 576, 320, 4),     # >16 rows per expert, K tails
+                                       (1, 16, 256, 128, 16),     # k = E, one token
+                                       (64, 4, 256, 192, 4)])     # k = E, 64 rows per expert
+def test_layer_ragged_shapes(T, E, H, I, k):
+    lw, x, logits = _case(21, T, E, H, I, k, e2m1_experts=(1,), permute="random")
+    out = run_layer(lw, x, logits, k)
+    ref = oracle.layer_forward(x, logits, k, lw)
+    check_layer(out, ref, k)
+
+
+def test_layer_residual_in_place():
+    mq = _mq()
+    T, E, H, I, k = 16, 4, 256, 128, 2
+    lw, x, logits = _case(22, T, E, H, I, k)
+    w = mq.DeviceWeights.from_host(lw)
+    L = mq.MoeLayer(T, H, I, E, k)
+    xb = dev(x.view(np.int16))
+    L.forward(xb, dev(logits), w, residual=xb, out=xb)        # y written over the residual
+    ref = oracle.layer_forward(x, logits, k, lw, residual_bits=x)
+    got = oracle.bf16_to_f64(u16(xb))
+    expect = oracle.bf16_to_f64(ref["x_next"])
+    rel = np.linalg.norm(got - expect, axis=1) / np.linalg.norm(expect, axis=1)
+    assert rel.max() < 5e-3
+
+
+def test_layer_invalid_expert_id_gives_nan_row():
+    mq = _mq()
+    T, E, H, I, k = 4, 4, 256, 128, 2
+    lw, x, logits = _case(23, T, E, H, I, k)
+    w = mq.DeviceWeights.from_host(lw)
+    L = mq.MoeLayer(T, H, I, E, k)
+    ids = np.array([[0, 1], [2, 9], [3, 0], [1, 2]], np.int32)
+    wts = np.full((T, k), 0.5, np.float32)
+    L.topk_ids.copy_(dev(ids.ravel()))
+    L.topk_w.copy_(dev(wts.ravel()))
+    L.permute()
+    L.gateup(dev(x.view(np.int16)), w)
+    L.down(w)
+    y = oracle.bf16_to_f64(u16(L.combine()))
+    assert host(L.offsets)[E] == 7
+    assert np.all(np.isnan(y[1])) and np.all(np.isfinite(y[[0, 2, 3]]))
+    ref = oracle.layer_forward(x, None, k, lw, routing=(ids.clip(0, E - 1),
+                                                        wts.astype(np.float64)))
+    rel = row_rel(u16(L.y)[[0, 2, 3]], ref["y"][[0, 2, 3]])
+    assert rel.max() < ROW_REL_TOL
+
+
+def test_layer_invalid_table_id_gives_nan_rows():
+    T, E, H, I, k = 16, 4, 256, 128, 2
+    lw, x, logits = _case(24, T, E, H, I, k)
+    lw.table_id[2] = 7                       # only 2 tables exist
+    out = run_layer(lw, x, logits, k)
+    ids = out["ids"]
+    y = oracle.bf16_to_f64(out["y"])
+    uses2 = (ids == 2).any(1)
+    assert uses2.any() and np.all(np.isnan(y[uses2])) and np.all(np.isfinite(y[~uses2]))
+
+
+def test_layer_deterministic():
+    T, E, H, I, k = 37, 8, 576, 320, 4
+    lw, x, logits = _case(25, T, E, H, I, k)
+    a = run_layer(lw, x, logits, k)
+    b = run_layer(lw, x, logits, k)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+# ----------------------------------------------------------------------------------------------
+# full GLM sizes
+# ----------------------------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def glm_layer():
+    c = synth.CONFIGS[2]
+    return synth.make_layer(2, c.E, c.H, c.I)
+
+
+def test_glm_decode_t8_full(glm_layer):
+    c = synth.CONFIGS[2]
+    x = synth.make_x(2, c.T, c.H)
+    logits = synth.make_logits(2, c.T, c.E)
+    out = run_layer(glm_layer, x, logits, c.k)
+    ref = oracle.layer_forward(x, logits, c.k, glm_layer)
+    check_layer(out, ref, c.k)
