@@ -15,6 +15,7 @@ import ctypes
 import os
 
 import numpy as np
+import torch  # noqa: F401  (loads the HIP runtime libmoeq links against before libmoeq itself)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoeq.so")

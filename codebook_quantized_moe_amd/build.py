@@ -13,9 +13,10 @@ LIB = os.path.join(HERE, "libmoeq.so")
 SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm_skinny.hip", "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CLANGXX = "/opt/rocm/llvm/bin/clang++"
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
@@ -23,19 +24,45 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+def hip_runtime_dir() -> str:
+    """Directory of the HIP runtime the process uses for device memory and streams.
+
+    The library links the same libamdhip64 as torch (torch ships its own copy): one HIP
+    runtime per process, so torch's pointers, streams and events are valid in libmoeq.
+    """
+    import torch
+    d = os.path.join(os.path.dirname(torch.__file__), "lib")
+    if os.path.exists(os.path.join(d, "libamdhip64.so")):
+        return d
+    return "/opt/rocm/lib"
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (proc.stdout + proc.stderr).splitlines()
                     if "packed-fp32-ops" not in l)
     if proc.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{out}")
+        raise RuntimeError(f"{cmd[0]} failed ({proc.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
+
+
+def build(verbose: bool = False) -> str:
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for s in SOURCES:
+        obj = os.path.join(objdir, s.replace(".hip", ".o"))
+        _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", obj], verbose)
+        objs.append(obj)
+    rt = hip_runtime_dir()
+    tmp = LIB + ".tmp"
+    # plain host link (no implicit -lamdhip64): the device code objects are embedded in the
+    # host objects and registered by their constructors
+    _run([CLANGXX, "-shared", "-fPIC", *objs, "-o", tmp,
+          os.path.join(rt, "libamdhip64.so"), f"-Wl,-rpath,{rt}"], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -28,6 +28,9 @@ int ok() {
     return MOEQ_OK;
 }
 
+// Reset this thread's sticky HIP error state, so that check_launch reports only our launch.
+void clear_hip_error() { (void)hipGetLastError(); }
+
 int check_launch(const char* what) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOEQ_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
@@ -36,15 +39,23 @@ int check_launch(const char* what) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; MI355X has 256). Read from the
+// device properties rather than an attribute enum, whose numbering is not stable across HIP
+// runtime releases; any failure falls back to 256 and leaves no error state behind.
 int cu_count() {
     static int cache[64] = {0};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        clear_hip_error();
+        return 256;
+    }
     if (cache[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
+        hipDeviceProp_t prop;
+        int n = 256;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0 &&
+            prop.multiProcessorCount <= 4096)
+            n = prop.multiProcessorCount;
+        clear_hip_error();
         cache[dev] = n;
     }
     return cache[dev];
@@ -109,6 +120,7 @@ int moeq_route_topk(const float* logits, int T, int E, int k, int gating, int32_
     if (gating != MOEQ_GATING_SOFTMAX_TOPK) return fail(MOEQ_EINVAL, "%s: unknown gating %d", w, gating);
     if (T == 0) return ok();
     if (!logits || !topk_ids || !topk_w) return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    clear_hip_error();
     launch_route_topk(logits, T, E, k, topk_ids, topk_w, (hipStream_t)stream);
     return check_launch(w);
 }
@@ -119,6 +131,7 @@ int moeq_permute_by_expert(const int32_t* topk_ids, int T, int k, int E, int32_t
     if (int r = check_sizes(w, T, k, E)) return r;
     if (!expert_offsets) return fail(MOEQ_EINVAL, "%s: expert_offsets is NULL", w);
     if (T > 0 && (!topk_ids || !sorted_pair || !pair_pos)) return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    clear_hip_error();
     launch_permute(topk_ids, T * k, E, expert_offsets, sorted_pair, pair_pos, (hipStream_t)stream);
     return check_launch(w);
 }
@@ -161,6 +174,7 @@ static int projection(const char* w, bool gateup, const uint16_t* act, int T, in
     a.K = gateup ? H : I;
     a.out_ld = gateup ? I : H;
     const long touched = (long)(E < T * k ? E : T * k);
+    clear_hip_error();
     launch_skinny(a, gateup, persistent_blocks(touched * (a.N / 16)), stream);
     return check_launch(w);
 }
@@ -196,6 +210,7 @@ int moeq_unpermute_combine(const float* yp, const int32_t* pair_pos, const int32
     if (!yp || !pair_pos || !expert_offsets || !y) return fail(MOEQ_EINVAL, "%s: null pointer", w);
     if (!aligned(yp, 16) || !aligned(y, 8) || (residual && !aligned(residual, 8)))
         return fail(MOEQ_EUNSUPPORTED, "%s: yp must be 16-byte aligned, y and residual 8-byte aligned", w);
+    clear_hip_error();
     launch_combine(yp, pair_pos, expert_offsets, T, k, E, H, residual, y, (hipStream_t)stream);
     return check_launch(w);
 }
@@ -214,6 +229,7 @@ int moeq_debug_dequant(const uint8_t* codes, const uint8_t* scales, int E, int N
     const size_t total = (size_t)E * N * (K / 8);
     size_t blocks = (total + 255) / 256;
     if (blocks > (size_t)cu_count() * 16) blocks = (size_t)cu_count() * 16;
+    clear_hip_error();
     launch_dequant(codes, scales, E, N, K, table_id, ta, out, (int)blocks, (hipStream_t)stream);
     return check_launch(w);
 }
