@@ -1,0 +1,219 @@
+"""Benchmark of the routed-expert MoE layer forward over 4-bit codebook experts on one MI355X.
+
+One step = one pass of the whole hot path (route -> permute -> gate|up+SwiGLU -> down ->
+unpermute/combine) over one batch of synthetic tokens, with inputs resident in HBM.
+
+Default workload: the GLM-shaped single-layer decode (hidden 6144, intermediate 2048,
+256 experts, top-8, 8 tokens), HBM-bound. Every step routes a fresh batch of tokens, and the
+steps rotate over several device copies of the layer's weights so that no step reads
+weights that the previous steps left in the ~256 MB last-level cache (MALL).
+
+Prints ONE JSON line. ``roofline`` covers the dominant kernel (the fused gate|up projection):
+algorithmic bytes (touched experts' gate+up codes and scales + activations in/out) per launch
+divided by its average launch time, measured with HIP events on the launch stream.
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+METRIC = "routed-MoE layer tokens/s; decode HBM GB/s and prefill MFMA util vs peak"
+
+
+def expert_bytes(H, I):
+    """Stored bytes of one expert: codes (4 bit/weight) + E8M0 scales (1 byte per 32)."""
+    gate_up = 2 * (I * H // 2 + I * H // 32)
+    down = H * I // 2 + H * I // 32
+    return gate_up, down
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 5])
+    ap.add_argument("--copies", type=int, default=4,
+                    help="device copies of the weights rotated over the steps (MALL-cold reads)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2,
+                    help="tokens of the workload the CPU oracle is timed on")
+    ap.add_argument("--pmc-calibrate", action="store_true",
+                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, lw, x, logits, n_tokens):
+    """The fp64 oracle, as it stands, on the first n_tokens tokens of one batch."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    toks = list(range(min(n_tokens, cfg.T)))
+    t0 = time.perf_counter()
+    oracle.layer_forward(x, logits, cfg.k, lw, tokens=toks)
+    dt = time.perf_counter() - t0
+    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(toks)} of the {cfg.T} tokens of one batch (all routing, the "
+                      f"sampled tokens' experts), {dt:.1f} s, numpy fp64 "
+                      f"(BLAS threads {threads}, os.cpu_count {os.cpu_count()})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is a design note, not a run.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import codebook_quantized_moe_amd as mq
+    import synth
+
+    cfg = synth.CONFIGS[args.config]
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    dev = torch.device("cuda")
+    t_gen = time.perf_counter()
+    lw = synth.make_layer(cfg.cfg_id, E, H, I, e2m1_experts=cfg.e2m1, permute=cfg.permute)
+    w0 = mq.DeviceWeights.from_host(lw)
+    copies = [w0]
+    decode = T * k <= 4 * E
+    ncopies = max(1, args.copies) if decode else 1
+    for _ in range(ncopies - 1):
+        copies.append(mq.DeviceWeights(*(t.clone() if torch.is_tensor(t) else t
+                                         for t in (w0.gate_codes, w0.gate_scales, w0.up_codes,
+                                                   w0.up_scales, w0.down_codes, w0.down_scales,
+                                                   w0.tables, w0.table_id))))
+    nb = args.warmup + args.steps
+    xs, lgs = [], []
+    for b in range(nb):
+        xs.append(synth.make_x(cfg.cfg_id, T, H, batch=b))
+        lgs.append(synth.make_logits(cfg.cfg_id, T, E, zipf_s=cfg.zipf_s, batch=b))
+    xd = [torch.from_numpy(x.view(np.int16)).to(dev) for x in xs]
+    ld = [torch.from_numpy(l).to(dev) for l in lgs]
+    L = mq.MoeLayer(T, H, I, E, k)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+
+    # touched experts (and padding-free rows) of every batch, from the library's own routing
+    touched = []
+    for b in range(nb):
+        L.route(ld[b])
+        L.permute()
+        off = L.offsets.cpu().numpy()
+        touched.append(int((np.diff(off) > 0).sum()))
+
+    def step(b):
+        w = copies[b % ncopies]
+        L.route(ld[b])
+        L.permute()
+        ev[b][0].record()
+        L.gateup(xd[b], w)
+        ev[b][1].record()
+        L.down(w)
+        ev[b][2].record()
+        L.combine()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nb)]
+    for b in range(args.warmup):
+        step(b)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for b in range(args.warmup, nb):
+        step(b)
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    timed = range(args.warmup, nb)
+    gu_ms = [ev[b][0].elapsed_time(ev[b][1]) for b in timed]
+    dn_ms = [ev[b][1].elapsed_time(ev[b][2]) for b in timed]
+
+    gu_w, dn_w = expert_bytes(H, I)
+    P = T * k
+    gu_bytes = [touched[b] * gu_w + T * H * 2 + P * I * 2 for b in timed]
+    dn_bytes = [touched[b] * dn_w + P * I * 2 + P * H * 4 + P * 4 for b in timed]
+    step_bytes = [touched[b] * (gu_w + dn_w) + T * E * 4 + 2 * T * H * 2 for b in timed]
+    flops_gu = 2.0 * P * 2 * I * H
+    flops_dn = 2.0 * P * H * I
+
+    ms_per_step = total_ms / args.steps
+    value = T * args.steps / (total_ms / 1e3)
+    gu_avg = float(np.mean(gu_ms))
+    if decode:
+        ach = float(np.mean(gu_bytes)) / (gu_avg / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        ach = flops_gu / (gu_avg / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "hidden": H, "intermediate": I,
+                   "experts": E, "top_k": k, "zipf_s": cfg.zipf_s,
+                   "e2m1_experts": list(cfg.e2m1), "channel_permutation": cfg.permute,
+                   "weight_copies": ncopies},
+        "roofline": roof,
+        "kernels": {
+            "gateup_swiglu": {"avg_us": round(gu_avg * 1e3, 2),
+                              "bytes_per_launch": int(np.mean(gu_bytes)),
+                              "GB_s": round(float(np.mean(gu_bytes)) / gu_avg / 1e6, 1),
+                              "TFLOP_s": round(flops_gu / gu_avg / 1e9, 2)},
+            "down": {"avg_us": round(float(np.mean(dn_ms)) * 1e3, 2),
+                     "bytes_per_launch": int(np.mean(dn_bytes)),
+                     "GB_s": round(float(np.mean(dn_bytes)) / float(np.mean(dn_ms)) / 1e6, 1),
+                     "TFLOP_s": round(flops_dn / float(np.mean(dn_ms)) / 1e9, 2)},
+        },
+        "layer": {"touched_experts_avg": round(float(np.mean([touched[b] for b in timed])), 2),
+                  "algorithmic_bytes_per_step": int(np.mean(step_bytes)),
+                  "step_GB_s": round(float(np.mean(step_bytes)) / ms_per_step / 1e6, 1),
+                  "step_hbm_frac": round(float(np.mean(step_bytes)) / ms_per_step / 1e6
+                                         / HBM_PEAK_GBS, 4),
+                  "step_TFLOP_s": round((flops_gu + flops_dn) / ms_per_step / 1e9, 2)},
+        "input_setup_s": round(t_gen, 1),
+    }
+
+    if args.pmc_calibrate:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        bcopy = torch.empty_like(a)
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+        out["pmc_calibration_copy_bytes"] = 256 << 20
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, lw, xs[0], lgs[0], args.cpu_tokens)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

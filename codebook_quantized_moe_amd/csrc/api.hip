@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "moeq.h"
@@ -95,12 +96,15 @@ int check_hk(const char* what, int H, int I) {
     return MOEQ_OK;
 }
 
-int persistent_blocks(long items) {
-    const long cap = (long)cu_count() * 8;
-    long b = (items + 3) / 4;
+// Workgroups of a persistent launch: enough to hold every item once, at most as many as are
+// resident at once (2 workgroups of 8 wavefronts per CU: 4 wavefronts per SIMD).
+int persistent_blocks(long wg_items) {
+    const long cap = (long)cu_count() * 2;
+    long b = wg_items;
     if (b > cap) b = cap;
     return (int)(b < 1 ? 1 : b);
 }
+
 
 }  // namespace
 
@@ -156,8 +160,13 @@ static int projection(const char* w, bool gateup, const uint16_t* act, int T, in
     const size_t need = moeq_workspace_bytes(T, k, E, H, I);
     if (need > 0 && (!ws || ws_bytes < need))
         return fail(MOEQ_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", w, need, ws_bytes);
+    const long long act_bytes = gateup ? (long long)T * H * 2 : (long long)T * k * I * 2;
+    const long long mat_bytes = gateup ? (long long)I * H / 2 : (long long)H * I / 2;
+    if (act_bytes >= (1LL << 31) || mat_bytes >= (1LL << 31))
+        return fail(MOEQ_EUNSUPPORTED, "%s: activations and each expert matrix must stay below 2 GiB", w);
     if (T == 0) return ok();
     a.act = act;
+    a.act_bytes = (uint32_t)act_bytes;
     a.offsets = offsets;
     a.sorted_pair = sorted_pair;
     a.topk_w = topk_w;
@@ -174,8 +183,12 @@ static int projection(const char* w, bool gateup, const uint16_t* act, int T, in
     a.K = gateup ? H : I;
     a.out_ld = gateup ? I : H;
     const long touched = (long)(E < T * k ? E : T * k);
+    // upper bound of the items (tile x column block) the device will find
+    const long tiles = touched + (long)T * k / decode_tile_rows();
+    const int cpw = decode_cols_per_wg(gateup);
+    const long items = tiles * ((a.N + cpw - 1) / cpw);
     clear_hip_error();
-    launch_skinny(a, gateup, persistent_blocks(touched * (a.N / 16)), stream);
+    launch_decode(a, gateup, persistent_blocks(items), stream);
     return check_launch(w);
 }
 

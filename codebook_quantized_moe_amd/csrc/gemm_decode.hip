@@ -1,0 +1,421 @@
+// Grouped projections for few rows per expert (decode): the expert weights are the traffic.
+//
+// MFMA shape. v_mfma_f32_4x4x4_16b_bf16 runs 16 independent 4x4x4 products; lane 4b + q holds
+// row q of block b's A (4 K values), column q of block b's B, and column q (rows 0..3) of
+// block b's result. The 16 blocks are used as 16 slices of K of one 4-row x 4-column product
+// and summed by a lane butterfly when an item is complete. A tile therefore has M = 4 token
+// rows (the size of an expert's share of a decode batch) instead of a 16-row operand that
+// would be mostly padding.
+//
+// Memory path. On MI355X the vector-memory address path, not HBM, bounds a weight stream that
+// is fetched with narrow or out-of-range loads: a wavefront instruction costs about the same
+// whether it moves 64 bytes or 1 KiB. So the hot loop issues only full 16-byte, in-range
+// loads of codes -- lane (b, q) reads 32 codes of weight row 4g + q at K 32b .. 32b + 31 of a
+// 512-wide K-step, one instruction per column group g covering 4 rows x 256 contiguous bytes,
+// with the non-temporal hint (each byte is read once) -- and everything else comes from LDS:
+//   * the tile's activation rows and the scale bytes of the workgroup's 128 weight rows are
+//     staged per 2048-wide K-chunk by the whole workgroup with 16-byte loads, double-buffered
+//     (one barrier per chunk), and shared by its 8 wavefronts;
+//   * the exact bf16 decode tables (one 16-byte entry per table and scale byte).
+// Codes of the next PF K-steps stay in flight per wavefront, across chunk and item boundaries.
+//
+// Work item = (tile of <= 4 sorted rows of one expert, block of 64 channels for gate|up or
+// 128 output rows for down); a workgroup (8 wavefronts) takes one item at a time, wavefront w
+// takes 16 weight rows of it over the whole K.
+// gate|up ("Round 7" brief, decision 4): wavefront w decodes the gate rows and the up rows of
+// the same 8 channels, so bf16(silu(g) * u) is formed in registers.
+// down ("Round 7" brief, decision 6; README "What had to be fixed": router weighting in the
+// down epilogue): writes topk_w[p] * (I . Wd) in fp32.
+// The grid is persistent; expert row counts are read from expert_offsets on the device.
+#include "moeq_device.h"
+#include "moeq_kernels.h"
+
+namespace moeq {
+
+constexpr int kDecWaves = 8;
+constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kTileRows = 4;
+constexpr int kStepK = 512;                       // K per step: lane b covers 32 codes
+constexpr int kChunkK = 2048;                     // K per staged chunk (4 steps)
+constexpr int kRowsPerWG = 16 * kDecWaves;        // weight rows per workgroup item
+constexpr int kARowUnits = kChunkK / 8 + 1;       // 16-byte units per staged row (+1: banks)
+constexpr int kABufBytes = kTileRows * kARowUnits * 16;
+constexpr int kSBufBytes = kRowsPerWG * (kChunkK / 32);
+constexpr uint32_t kOutOfRange = 0x80000000u;
+// non-temporal: the weight streams are read once (a plain read kernel reaches ~4.9 TB/s
+// with the default policy and ~6.8 TB/s with this hint on MI355X)
+constexpr int kStreamPolicy = 2;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+template <int POLICY>
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
+}
+
+__device__ __forceinline__ f32x4 mfma4x4x4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
+                                           f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, u32x2{a0, a1}),
+                                                  __builtin_bit_cast(s16x4, u32x2{b0, b1}), c, 0,
+                                                  0, 0);
+}
+
+// Active experts (ascending) and the prefix count of their kTileRows-row tiles, in LDS.
+// Returns the count of active experts; tpre[count] is the number of tiles. All threads.
+__device__ inline int active_tiles(const int32_t* offsets, int E, int* active, int* tpre,
+                                   int* n_s) {
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x < 64) {
+        int rows[4], c = 0, nt = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = lane * 4 + j;
+            rows[j] = e < E ? offsets[e + 1] - offsets[e] : 0;
+            c += rows[j] > 0;
+            nt += (rows[j] + kTileRows - 1) / kTileRows;
+        }
+        int ic = c, it = nt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int oc = __shfl_up(ic, off, 64), ot = __shfl_up(it, off, 64);
+            if (lane >= off) { ic += oc; it += ot; }
+        }
+        int pos = ic - c, pre = it - nt;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (rows[j] > 0) {
+                active[pos] = lane * 4 + j;
+                tpre[pos] = pre;
+                ++pos;
+                pre += (rows[j] + kTileRows - 1) / kTileRows;
+            }
+        if (lane == 63) {
+            *n_s = ic;
+            tpre[ic] = it;
+        }
+    }
+    __syncthreads();
+    return *n_s;
+}
+
+struct Item {
+    int e, cb, r0, rows;
+};
+
+__device__ __forceinline__ Item locate(long item, int ncb, int nact, const int* active,
+                                       const int* tpre, const int32_t* offsets) {
+    Item it;
+    const int tile = (int)(item / ncb);
+    it.cb = (int)(item % ncb);
+    int lo = 0, hi = nact - 1;                    // last a with tpre[a] <= tile
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tpre[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    it.e = __builtin_amdgcn_readfirstlane(active[lo]);
+    const int m0 = (tile - __builtin_amdgcn_readfirstlane(tpre[lo])) * kTileRows;
+    const int beg = __builtin_amdgcn_readfirstlane(offsets[it.e]);
+    const int end = __builtin_amdgcn_readfirstlane(offsets[it.e + 1]);
+    it.r0 = beg + m0;
+    it.rows = min(kTileRows, end - it.r0);
+    return it;
+}
+
+// Weight row (within its matrix) of column group g, lane q, wavefront w; mat = 1 for up rows.
+template <bool GATEUP>
+__device__ __forceinline__ int weight_row(int cb, int w, int g, int q, int* mat) {
+    if (GATEUP) {
+        *mat = g >> 1;
+        return cb * 64 + w * 8 + (g & 1) * 4 + q;
+    }
+    *mat = 0;
+    return cb * kRowsPerWG + w * 16 + g * 4 + q;
+}
+
+template <bool GATEUP, int PF>
+__global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+decode_kernel(const SkinnyArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ int active[256];
+    __shared__ int tpre[257];
+    __shared__ int n_active_s;
+    u32x4* tab = reinterpret_cast<u32x4*>(smem);
+    uint8_t* abuf = smem + (size_t)a.tables.n * 256 * 16;
+    uint8_t* sbuf = abuf + 2 * kABufBytes;
+    build_decode_tables(a.tables, tab);
+    const int nact = active_tiles(a.offsets, a.E, active, tpre, &n_active_s);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int b = lane >> 2, q = lane & 3;
+    const int K = a.K, N = a.N;
+    const int ncb = GATEUP ? (N + 63) / 64 : (N + kRowsPerWG - 1) / kRowsPerWG;
+    const long items = (long)__builtin_amdgcn_readfirstlane(tpre[nact]) * ncb;
+    const int nsteps = (K + kStepK - 1) / kStepK;
+    const long first = blockIdx.x, stride = gridDim.x;
+    const long nmine = items > first ? (items - first + stride - 1) / stride : 0;
+    const long total = nmine * nsteps;
+    if (total == 0) return;                       // uniform per workgroup
+    const uint32_t kb = (uint32_t)K / 2, ks = (uint32_t)K / 32;
+    const uint32_t mc = (uint32_t)N * kb, ms = (uint32_t)N * ks;
+    const __amdgpu_buffer_rsrc_t ract = make_rsrc(a.act, a.act_bytes);
+
+    // ---------------- code stream (per wavefront, PF K-steps ahead) ----------------
+    struct CodeSrc {
+        __amdgpu_buffer_rsrc_t r0, r1;           // gate (or down) and up codes of the expert
+        uint32_t off[4];                         // byte offset of this lane's row, per group
+    };
+    auto code_src = [&](long item) {
+        const Item it = locate(item, ncb, nact, active, tpre, a.offsets);
+        CodeSrc s;
+        s.r0 = make_rsrc(a.codes0 + (size_t)it.e * mc, mc);
+        s.r1 = GATEUP ? make_rsrc(a.codes1 + (size_t)it.e * mc, mc) : s.r0;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            int mat;
+            const int row = weight_row<GATEUP>(it.cb, wave, g, q, &mat);
+            s.off[g] = row < N ? (uint32_t)row * kb + (uint32_t)b * 16 : kOutOfRange;
+        }
+        return s;
+    };
+    long l_item = first;
+    int l_step = 0;
+    CodeSrc lsrc = code_src(l_item);
+    auto load_codes = [&]() {
+        const int kk = l_step * kStepK;
+        const bool ok = l_item < items && kk + b * 32 < K;
+        u32x4 c[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint32_t off = (ok && lsrc.off[g] != kOutOfRange) ? lsrc.off[g] + kk / 2
+                                                                     : kOutOfRange;
+            c[g] = bload16<kStreamPolicy>((GATEUP && g >= 2) ? lsrc.r1 : lsrc.r0, off);
+        }
+        if (++l_step == nsteps) {
+            l_step = 0;
+            l_item += stride;
+            if (l_item < items) lsrc = code_src(l_item);
+        }
+        struct R { u32x4 c[4]; } r;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) r.c[g] = c[g];
+        return r;
+    };
+
+    // ---------------- staging of activations and scales (per workgroup, per chunk) -------
+    struct Stage {
+        u32x4 x0, x1, s;
+    };
+    const int sa_row = tid >> 7, sa_p = tid & 127;           // activation: row, 16-byte piece
+    const int ss_row = tid >> 2, ss_p = tid & 3;             // scales: row (of 128), piece
+    auto stage_load = [&](long item, int chunk) {
+        Stage st;
+        const Item it = locate(item, ncb, nact, active, tpre, a.offsets);
+        const int kc = chunk * kChunkK;
+        // activations: tile row sa_row, elements kc + 8 p .. + 7 for p = sa_p, sa_p + 128
+        uint32_t ab = kOutOfRange;
+        if (sa_row < it.rows) {
+            const uint32_t src = GATEUP ? (uint32_t)(a.sorted_pair[it.r0 + sa_row] / a.k)
+                                        : (uint32_t)(it.r0 + sa_row);
+            ab = src * (uint32_t)K * 2u;
+        }
+        const int k0 = kc + sa_p * 8, k1 = kc + (sa_p + 128) * 8;
+        st.x0 = bload16<0>(ract, (ab != kOutOfRange && k0 < K) ? ab + (uint32_t)k0 * 2u : kOutOfRange);
+        st.x1 = bload16<0>(ract, (ab != kOutOfRange && k1 < K) ? ab + (uint32_t)k1 * 2u : kOutOfRange);
+        // scales: weight row ss_row of the item, bytes kc/32 + 16 p .. + 15
+        const int w = ss_row >> 4, g = (ss_row >> 2) & 3, qq = ss_row & 3;
+        int mat;
+        const int row = weight_row<GATEUP>(it.cb, w, g, qq, &mat);
+        const int sb = kc / 32 + ss_p * 16;                  // first scale byte of the piece
+        const int valid = min(16, (int)ks - sb);             // bytes of this row in range
+        u32x4 sv = {0, 0, 0, 0};
+        if (row < N && valid > 0) {
+            const uint8_t* sbase = (mat ? a.scales1 : a.scales0) + (size_t)it.e * ms;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(sbase, ms);
+            // a row of K/32 scale bytes is only 2-byte aligned in general: load the dwords
+            // around it from the 4-byte boundary below and shift the bytes into place
+            const uint32_t off = (uint32_t)row * ks + (uint32_t)sb;
+            const u32x4 lo = bload16<kStreamPolicy>(rs, off & ~3u);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(rs, (off & ~3u) + 16, 0,
+                                                                    kStreamPolicy);
+            const uint32_t sh = off & 3u;
+            sv = u32x4{__builtin_amdgcn_alignbyte(lo[1], lo[0], sh),
+                       __builtin_amdgcn_alignbyte(lo[2], lo[1], sh),
+                       __builtin_amdgcn_alignbyte(lo[3], lo[2], sh),
+                       __builtin_amdgcn_alignbyte(hi, lo[3], sh)};
+            // bytes past the row's end belong to the next row: clear them (K tail)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int nb = valid - 4 * j;
+                if (nb <= 0) sv[j] = 0;
+                else if (nb < 4) sv[j] &= (1u << (8 * nb)) - 1u;
+            }
+        }
+        st.s = sv;
+        return st;
+    };
+    auto stage_store = [&](const Stage& st, int buf) {
+        uint8_t* ab = abuf + buf * kABufBytes + sa_row * kARowUnits * 16;
+        const u32x4 x0 = GATEUP ? pair_split(st.x0) : st.x0;   // x arrives in natural order
+        const u32x4 x1 = GATEUP ? pair_split(st.x1) : st.x1;
+        *reinterpret_cast<u32x4*>(ab + sa_p * 16) = x0;
+        *reinterpret_cast<u32x4*>(ab + (sa_p + 128) * 16) = x1;
+        *reinterpret_cast<u32x4*>(sbuf + buf * kSBufBytes + ss_row * (kChunkK / 32) + ss_p * 16) =
+            st.s;
+    };
+
+    // first chunk of the first item, synchronously
+    const int nchunks = (K + kChunkK - 1) / kChunkK;
+    {
+        const Stage st = stage_load(first, 0);
+        stage_store(st, 0);
+    }
+    __syncthreads();
+
+    struct Ring { u32x4 c[4]; };
+    Ring ring[PF + 1];
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+        auto r = load_codes();
+#pragma unroll
+        for (int g = 0; g < 4; ++g) ring[u].c[g] = r.c[g];
+    }
+
+    // staging cursor: the chunk after the one being computed
+    long s_item = first;
+    int s_chunk = 0;
+    auto advance_chunk = [&](long& item, int& chunk) {
+        if (++chunk == nchunks) { chunk = 0; item += stride; }
+    };
+    advance_chunk(s_item, s_chunk);
+    int buf = 0;                                  // buffer of the chunk being computed
+    Stage pending;
+
+    Item cp;
+    const u32x4* mytab = tab;
+    bool badtab = false;
+    f32x4 acc[4];
+    long c_item = first;
+    int c_step = 0;
+
+    for (long q0 = 0; q0 < total; q0 += PF + 1) {
+#pragma unroll
+        for (int u = 0; u < PF + 1; ++u) {
+            if (q0 + u >= total) break;
+            if (c_step == 0) {
+                cp = locate(c_item, ncb, nact, active, tpre, a.offsets);
+                const int tsel = a.table_id[cp.e];
+                badtab = tsel >= a.tables.n;
+                mytab = tab + (badtab ? 0 : tsel) * 256;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            const int kk = c_step * kStepK;
+            const int sub = (kk % kChunkK) / kStepK;
+            const int chunk_end = min(nsteps, (kk / kChunkK + 1) * (kChunkK / kStepK));
+            const bool last_in_chunk = c_step + 1 == chunk_end;
+            const bool more = s_item < first + nmine * stride;   // a next chunk exists
+            if (sub == 0 && more) pending = stage_load(s_item, s_chunk);
+            {
+                auto r = load_codes();
+#pragma unroll
+                for (int g = 0; g < 4; ++g) ring[(u + PF) % (PF + 1)].c[g] = r.c[g];
+            }
+            const Ring& cur = ring[u];
+            // activation operands: tile row q, K 32 b .. 32 b + 31 of the step (pair-split)
+            const uint8_t* ap = abuf + buf * kABufBytes + q * kARowUnits * 16 +
+                                ((kk % kChunkK) / 8 + b * 4) * 16;
+            u32x4 A[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) A[j] = *reinterpret_cast<const u32x4*>(ap + 16 * j);
+            const uint8_t* sp = sbuf + buf * kSBufBytes + (wave * 16 + q) * (kChunkK / 32) +
+                                (kk % kChunkK) / 32 + b;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint32_t s = sp[g * 4 * (kChunkK / 32)];
+                const u32x4 t = mytab[s];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const u32x4 w = decode8(cur.c[g][j], t);
+                    acc[g] = mfma4x4x4(A[j][0], A[j][1], w[0], w[1], acc[g]);
+                    acc[g] = mfma4x4x4(A[j][2], A[j][3], w[2], w[3], acc[g]);
+                }
+            }
+            if (last_in_chunk) {
+                if (more) {
+                    stage_store(pending, buf ^ 1);
+                    advance_chunk(s_item, s_chunk);
+                }
+                __syncthreads();
+                buf ^= 1;
+            }
+            if (++c_step < nsteps) continue;
+            // ---- item complete: sum the 16 K-slices (lanes q, q + 4, ..., q + 60) ----
+            c_step = 0;
+            c_item += stride;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = acc[g][r];
+                    v += __shfl_xor(v, 4, 64);
+                    v += __shfl_xor(v, 8, 64);
+                    v += __shfl_xor(v, 16, 64);
+                    v += __shfl_xor(v, 32, 64);
+                    acc[g][r] = v;
+                }
+            if (lane >= 4) continue;
+            // lane q holds rows 0..3 of this wavefront's columns 4 g + q
+            if (GATEUP) {
+                uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int ch = cp.cb * 64 + wave * 8 + h * 4 + q;
+                    if (ch >= N) continue;
+                    const int slot = (ch & ~7) | (((ch & 1) << 2) | ((ch & 7) >> 1));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (r >= cp.rows) continue;
+                        const float v = badtab ? __builtin_nanf("")
+                                               : silu_mul(acc[h][r], acc[2 + h][r]);
+                        out[(size_t)(cp.r0 + r) * a.out_ld + slot] = (uint16_t)f32_to_bf16_rne(v);
+                    }
+                }
+            } else {
+                float* out = reinterpret_cast<float*>(a.out);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (r >= cp.rows) continue;
+                    const size_t row = (size_t)(cp.r0 + r);
+                    const float wgt = a.topk_w[a.sorted_pair[row]];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int col = cp.cb * kRowsPerWG + wave * 16 + g * 4 + q;
+                        if (col >= N) continue;
+                        out[row * a.out_ld + col] = badtab ? __builtin_nanf("") : wgt * acc[g][r];
+                    }
+                }
+            }
+        }
+    }
+}
+
+int decode_tile_rows() { return kTileRows; }
+int decode_cols_per_wg(bool gateup) { return gateup ? 64 : kRowsPerWG; }
+
+void launch_decode(const SkinnyArgs& a, bool gateup, int blocks, hipStream_t stream) {
+    const size_t lds = (size_t)a.tables.n * 256 * 16 + 2 * kABufBytes + 2 * kSBufBytes;
+    constexpr int PF = 2;
+    if (gateup)
+        hipLaunchKernelGGL((decode_kernel<true, PF>), dim3(blocks), dim3(kDecThreads), lds, stream, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<false, PF>), dim3(blocks), dim3(kDecThreads), lds, stream, a);
+}
+
+}  // namespace moeq

@@ -109,9 +109,9 @@ def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16).copy()
 
 
-def make_x(cfg_id: int, T: int, H: int, layer: int = 0) -> np.ndarray:
+def make_x(cfg_id: int, T: int, H: int, layer: int = 0, batch: int = 0) -> np.ndarray:
     """bf16 bits [T, H] from N(0, 1)."""
-    x = rng(cfg_id, S_X, layer).standard_normal((T, H), dtype=np.float32)
+    x = rng(cfg_id, S_X, layer, batch).standard_normal((T, H), dtype=np.float32)
     return bf16_bits_from_f32(x)
 
 
@@ -122,9 +122,10 @@ def zipf_bias(cfg_id: int, E: int, s: float, layer: int = 0) -> np.ndarray:
 
 
 def make_logits(cfg_id: int, T: int, E: int, layer: int = 0, zipf_s: float | None = None,
-                distinct: bool = True) -> np.ndarray:
-    """fp32 [T, E] router logits N(0, 1) (+ Zipf bias); rows redrawn until values are distinct."""
-    g = rng(cfg_id, S_LOGITS, layer)
+                distinct: bool = True, batch: int = 0) -> np.ndarray:
+    """fp32 [T, E] router logits N(0, 1) (+ the layer's Zipf bias); rows redrawn until their
+    values are distinct. ``batch`` selects an independent batch of tokens of the same layer."""
+    g = rng(cfg_id, S_LOGITS, layer, batch)
     z = g.standard_normal((T, E), dtype=np.float32)
     if zipf_s is not None:
         z = (z + zipf_bias(cfg_id, E, zipf_s, layer)[None, :]).astype(np.float32)
