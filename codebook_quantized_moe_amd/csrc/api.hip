@@ -98,6 +98,17 @@ int check_hk(const char* what, int H, int I) {
 
 // Workgroups of a persistent launch: enough to hold every item once, at most as many as are
 // resident at once (2 workgroups of 8 wavefronts per CU: 4 wavefronts per SIMD).
+// Which projection kernels run: the prefill kernels (128-row MFMA tiles, weights decoded into
+// LDS once per tile) when experts get many rows on average, the decode kernels (4-row tiles,
+// weights decoded in registers, one pass over the weights) otherwise. MOEQ_FORCE_PATH=decode
+// or prefill overrides the choice (both are exact; used to test each on the same inputs).
+bool use_prefill_path(int T, int k, int E) {
+    const char* f = getenv("MOEQ_FORCE_PATH");
+    if (f && strcmp(f, "decode") == 0) return false;
+    if (f && strcmp(f, "prefill") == 0) return true;
+    return (long long)T * k >= 16LL * E;     // >= 16 rows per expert on average
+}
+
 int persistent_blocks(long wg_items) {
     const long cap = (long)cu_count() * 2;
     long b = wg_items;
@@ -183,12 +194,17 @@ static int projection(const char* w, bool gateup, const uint16_t* act, int T, in
     a.K = gateup ? H : I;
     a.out_ld = gateup ? I : H;
     const long touched = (long)(E < T * k ? E : T * k);
-    // upper bound of the items (tile x column block) the device will find
-    const long tiles = touched + (long)T * k / decode_tile_rows();
-    const int cpw = decode_cols_per_wg(gateup);
-    const long items = tiles * ((a.N + cpw - 1) / cpw);
     clear_hip_error();
-    launch_decode(a, gateup, persistent_blocks(items), stream);
+    if (use_prefill_path(T, k, E)) {
+        // upper bound of the 128-row tiles the device will find
+        const long tiles = touched + (long)T * k / prefill_tile_rows();
+        launch_prefill(a, gateup, tiles, cu_count(), stream);
+    } else {
+        // upper bound of the 4-row tiles the device will find
+        const long tiles = touched + (long)T * k / decode_tile_rows();
+        const char* shape_env = getenv("MOEQ_DECODE_SHAPE");   // tuning only (0..4)
+        launch_decode(a, gateup, tiles, cu_count(), shape_env ? atoi(shape_env) : 0, stream);
+    }
     return check_launch(w);
 }
 

@@ -30,17 +30,28 @@
 #include "moeq_device.h"
 #include "moeq_kernels.h"
 
+#include <algorithm>
+
 namespace moeq {
 
-constexpr int kDecWaves = 8;
-constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kTileRows = 4;
 constexpr int kStepK = 512;                       // K per step: lane b covers 32 codes
-constexpr int kChunkK = 2048;                     // K per staged chunk (4 steps)
-constexpr int kRowsPerWG = 16 * kDecWaves;        // weight rows per workgroup item
-constexpr int kARowUnits = kChunkK / 8 + 1;       // 16-byte units per staged row (+1: banks)
-constexpr int kABufBytes = kTileRows * kARowUnits * 16;
-constexpr int kSBufBytes = kRowsPerWG * (kChunkK / 32);
+
+// Shape of a decode launch: WAVES wavefronts per workgroup (16 weight rows each), K staged
+// in chunks of CHUNK.
+#define GATEUP_COLS(w) (8 * (w))
+template <int WAVES, int CHUNK>
+struct DecShape {
+    static constexpr int kWaves = WAVES;
+    static constexpr int kThreads = 64 * WAVES;
+    static constexpr int kChunkK = CHUNK;
+    static constexpr int kRowsPerWG = 16 * WAVES;                 // weight rows per item
+    static constexpr int kChannelsPerWG = GATEUP_COLS(WAVES);   // gate|up channels per item
+    static constexpr int kARowUnits = CHUNK / 8 + 1;              // 16-byte units per row (+1)
+    static constexpr int kABufBytes = kTileRows * kARowUnits * 16;
+    static constexpr int kSBufBytes = kRowsPerWG * (CHUNK / 32);
+};
+
 constexpr uint32_t kOutOfRange = 0x80000000u;
 // non-temporal: the weight streams are read once (a plain read kernel reaches ~4.9 TB/s
 // with the default policy and ~6.8 TB/s with this hint on MI355X)
@@ -128,19 +139,22 @@ __device__ __forceinline__ Item locate(long item, int ncb, int nact, const int* 
 }
 
 // Weight row (within its matrix) of column group g, lane q, wavefront w; mat = 1 for up rows.
-template <bool GATEUP>
+template <bool GATEUP, class S>
 __device__ __forceinline__ int weight_row(int cb, int w, int g, int q, int* mat) {
     if (GATEUP) {
         *mat = g >> 1;
-        return cb * 64 + w * 8 + (g & 1) * 4 + q;
+        return cb * S::kChannelsPerWG + w * 8 + (g & 1) * 4 + q;
     }
     *mat = 0;
-    return cb * kRowsPerWG + w * 16 + g * 4 + q;
+    return cb * S::kRowsPerWG + w * 16 + g * 4 + q;
 }
 
-template <bool GATEUP, int PF>
-__global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+template <bool GATEUP, int PF, class S>
+__global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 decode_kernel(const SkinnyArgs a) {
+    constexpr int kChunkK = S::kChunkK, kRowsPerWG = S::kRowsPerWG;
+    constexpr int kARowUnits = S::kARowUnits, kABufBytes = S::kABufBytes;
+    constexpr int kSBufBytes = S::kSBufBytes;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int active[256];
     __shared__ int tpre[257];
@@ -155,7 +169,8 @@ decode_kernel(const SkinnyArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = lane >> 2, q = lane & 3;
     const int K = a.K, N = a.N;
-    const int ncb = GATEUP ? (N + 63) / 64 : (N + kRowsPerWG - 1) / kRowsPerWG;
+    const int ncb = GATEUP ? (N + S::kChannelsPerWG - 1) / S::kChannelsPerWG
+                           : (N + kRowsPerWG - 1) / kRowsPerWG;
     const long items = (long)__builtin_amdgcn_readfirstlane(tpre[nact]) * ncb;
     const int nsteps = (K + kStepK - 1) / kStepK;
     const long first = blockIdx.x, stride = gridDim.x;
@@ -179,7 +194,7 @@ decode_kernel(const SkinnyArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             int mat;
-            const int row = weight_row<GATEUP>(it.cb, wave, g, q, &mat);
+            const int row = weight_row<GATEUP, S>(it.cb, wave, g, q, &mat);
             s.off[g] = row < N ? (uint32_t)row * kb + (uint32_t)b * 16 : kOutOfRange;
         }
         return s;
@@ -209,33 +224,45 @@ decode_kernel(const SkinnyArgs a) {
     };
 
     // ---------------- staging of activations and scales (per workgroup, per chunk) -------
+    // staging: activations are kTileRows rows x (kChunkK / 8) 16-byte pieces, scales are
+    // kRowsPerWG rows x (kChunkK / 512) 16-byte pieces
+    constexpr int kAPieces = kTileRows * (kChunkK / 8);
+    constexpr int kAPerThread = kAPieces / S::kThreads;
+    constexpr int kSPiecesPerRow = kChunkK / 512;
+    static_assert(kAPieces % S::kThreads == 0, "activation staging");
+    static_assert(kRowsPerWG * kSPiecesPerRow <= S::kThreads, "scale staging: <= 1 piece per thread");
+    const bool s_thread = tid < kRowsPerWG * kSPiecesPerRow;
     struct Stage {
-        u32x4 x0, x1, s;
+        u32x4 x[kAPerThread];
+        u32x4 s;
     };
-    const int sa_row = tid >> 7, sa_p = tid & 127;           // activation: row, 16-byte piece
-    const int ss_row = tid >> 2, ss_p = tid & 3;             // scales: row (of 128), piece
+    const int ss_row = tid / kSPiecesPerRow, ss_p = tid % kSPiecesPerRow;
     auto stage_load = [&](long item, int chunk) {
         Stage st;
         const Item it = locate(item, ncb, nact, active, tpre, a.offsets);
         const int kc = chunk * kChunkK;
-        // activations: tile row sa_row, elements kc + 8 p .. + 7 for p = sa_p, sa_p + 128
-        uint32_t ab = kOutOfRange;
-        if (sa_row < it.rows) {
-            const uint32_t src = GATEUP ? (uint32_t)(a.sorted_pair[it.r0 + sa_row] / a.k)
-                                        : (uint32_t)(it.r0 + sa_row);
-            ab = src * (uint32_t)K * 2u;
+        // activations: piece i = tid + j * threads -> tile row i / (kChunkK / 8), elements
+        // kc + 8 (i % (kChunkK / 8)) .. + 7
+#pragma unroll
+        for (int j = 0; j < kAPerThread; ++j) {
+            const int i = tid + j * S::kThreads;
+            const int row = i / (kChunkK / 8), k0 = kc + (i % (kChunkK / 8)) * 8;
+            uint32_t off = kOutOfRange;
+            if (row < it.rows && k0 < K) {
+                const uint32_t src = GATEUP ? (uint32_t)(a.sorted_pair[it.r0 + row] / a.k)
+                                            : (uint32_t)(it.r0 + row);
+                off = (src * (uint32_t)K + (uint32_t)k0) * 2u;
+            }
+            st.x[j] = bload16<0>(ract, off);
         }
-        const int k0 = kc + sa_p * 8, k1 = kc + (sa_p + 128) * 8;
-        st.x0 = bload16<0>(ract, (ab != kOutOfRange && k0 < K) ? ab + (uint32_t)k0 * 2u : kOutOfRange);
-        st.x1 = bload16<0>(ract, (ab != kOutOfRange && k1 < K) ? ab + (uint32_t)k1 * 2u : kOutOfRange);
         // scales: weight row ss_row of the item, bytes kc/32 + 16 p .. + 15
         const int w = ss_row >> 4, g = (ss_row >> 2) & 3, qq = ss_row & 3;
         int mat;
-        const int row = weight_row<GATEUP>(it.cb, w, g, qq, &mat);
+        const int row = weight_row<GATEUP, S>(it.cb, w, g, qq, &mat);
         const int sb = kc / 32 + ss_p * 16;                  // first scale byte of the piece
         const int valid = min(16, (int)ks - sb);             // bytes of this row in range
         u32x4 sv = {0, 0, 0, 0};
-        if (row < N && valid > 0) {
+        if (s_thread && row < N && valid > 0) {
             const uint8_t* sbase = (mat ? a.scales1 : a.scales0) + (size_t)it.e * ms;
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(sbase, ms);
             // a row of K/32 scale bytes is only 2-byte aligned in general: load the dwords
@@ -261,13 +288,16 @@ decode_kernel(const SkinnyArgs a) {
         return st;
     };
     auto stage_store = [&](const Stage& st, int buf) {
-        uint8_t* ab = abuf + buf * kABufBytes + sa_row * kARowUnits * 16;
-        const u32x4 x0 = GATEUP ? pair_split(st.x0) : st.x0;   // x arrives in natural order
-        const u32x4 x1 = GATEUP ? pair_split(st.x1) : st.x1;
-        *reinterpret_cast<u32x4*>(ab + sa_p * 16) = x0;
-        *reinterpret_cast<u32x4*>(ab + (sa_p + 128) * 16) = x1;
-        *reinterpret_cast<u32x4*>(sbuf + buf * kSBufBytes + ss_row * (kChunkK / 32) + ss_p * 16) =
-            st.s;
+#pragma unroll
+        for (int j = 0; j < kAPerThread; ++j) {
+            const int i = tid + j * S::kThreads;
+            const int row = i / (kChunkK / 8), p = i % (kChunkK / 8);
+            const u32x4 x = GATEUP ? pair_split(st.x[j]) : st.x[j];   // x arrives natural
+            *reinterpret_cast<u32x4*>(abuf + buf * kABufBytes + (row * kARowUnits + p) * 16) = x;
+        }
+        if (s_thread)
+            *reinterpret_cast<u32x4*>(sbuf + buf * kSBufBytes + ss_row * (kChunkK / 32) +
+                                      ss_p * 16) = st.s;
     };
 
     // first chunk of the first item, synchronously
@@ -376,7 +406,7 @@ decode_kernel(const SkinnyArgs a) {
                 uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const int ch = cp.cb * 64 + wave * 8 + h * 4 + q;
+                    const int ch = cp.cb * S::kChannelsPerWG + wave * 8 + h * 4 + q;
                     if (ch >= N) continue;
                     const int slot = (ch & ~7) | (((ch & 1) << 2) | ((ch & 7) >> 1));
 #pragma unroll
@@ -406,16 +436,34 @@ decode_kernel(const SkinnyArgs a) {
     }
 }
 
-int decode_tile_rows() { return kTileRows; }
-int decode_cols_per_wg(bool gateup) { return gateup ? 64 : kRowsPerWG; }
-
-void launch_decode(const SkinnyArgs& a, bool gateup, int blocks, hipStream_t stream) {
-    const size_t lds = (size_t)a.tables.n * 256 * 16 + 2 * kABufBytes + 2 * kSBufBytes;
+template <class S>
+static void launch_shape(const SkinnyArgs& a, bool gateup, long items, int cus, hipStream_t stream) {
+    const size_t lds = (size_t)a.tables.n * 256 * 16 + 2 * S::kABufBytes + 2 * S::kSBufBytes;
     constexpr int PF = 2;
+    const int per_cu = 16 / S::kWaves;                    // 4 wavefronts per SIMD
+    const long blocks = std::max(1L, std::min(items, (long)cus * per_cu));
     if (gateup)
-        hipLaunchKernelGGL((decode_kernel<true, PF>), dim3(blocks), dim3(kDecThreads), lds, stream, a);
+        hipLaunchKernelGGL((decode_kernel<true, PF, S>), dim3(blocks), dim3(S::kThreads), lds,
+                           stream, a);
     else
-        hipLaunchKernelGGL((decode_kernel<false, PF>), dim3(blocks), dim3(kDecThreads), lds, stream, a);
+        hipLaunchKernelGGL((decode_kernel<false, PF, S>), dim3(blocks), dim3(S::kThreads), lds,
+                           stream, a);
+}
+
+int decode_tile_rows() { return kTileRows; }
+
+// shape 0: 8 wavefronts, 2048-wide chunks; 1: 4 wavefronts, 2048; 2: 8 wavefronts, 1024;
+// 3: 4 wavefronts, 1024; 4: 16 wavefronts, 2048
+void launch_decode(const SkinnyArgs& a, bool gateup, long tiles, int cus, int shape,
+                   hipStream_t stream) {
+    auto items = [&](int cols) { return tiles * ((a.N + cols - 1) / cols); };
+    switch (shape) {
+    case 1: launch_shape<DecShape<4, 2048>>(a, gateup, items(gateup ? 32 : 64), cus, stream); break;
+    case 2: launch_shape<DecShape<8, 1024>>(a, gateup, items(gateup ? 64 : 128), cus, stream); break;
+    case 3: launch_shape<DecShape<4, 1024>>(a, gateup, items(gateup ? 32 : 64), cus, stream); break;
+    case 4: launch_shape<DecShape<16, 2048>>(a, gateup, items(gateup ? 128 : 256), cus, stream); break;
+    default: launch_shape<DecShape<8, 2048>>(a, gateup, items(gateup ? 64 : 128), cus, stream); break;
+    }
 }
 
 }  // namespace moeq

@@ -31,9 +31,11 @@ void launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, f
                        hipStream_t stream);
 void launch_permute(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pair,
                     int32_t* pair_pos, hipStream_t stream);
-void launch_decode(const SkinnyArgs& a, bool gateup, int blocks, hipStream_t stream);
+void launch_decode(const SkinnyArgs& a, bool gateup, long tiles, int cus, int shape,
+                   hipStream_t stream);
 int decode_tile_rows();
-int decode_cols_per_wg(bool gateup);
+void launch_prefill(const SkinnyArgs& a, bool gateup, long tiles, int cus, hipStream_t stream);
+int prefill_tile_rows();
 void launch_combine(const float* yp, const int32_t* pair_pos, const int32_t* offsets, int T, int k,
                     int E, int H, const uint16_t* residual, uint16_t* y, hipStream_t stream);
 void launch_dequant(const uint8_t* codes, const uint8_t* scales, int E, int N, int K,

@@ -23,6 +23,13 @@ def _gpu():
     import codebook_quantized_moe_amd  # noqa: F401  (fails loudly when not built)
 
 
+@pytest.fixture(params=["decode", "prefill"])
+def path(request, monkeypatch):
+    """Run the projections through the decode kernels or the prefill kernels."""
+    monkeypatch.setenv("MOEQ_FORCE_PATH", request.param)
+    return request.param
+
+
 def _mq():
     import codebook_quantized_moe_amd as mq
     return mq
@@ -195,7 +202,7 @@ def _case(cfg_id, T, E, H, I, k, **kw):
     return lw, x, logits
 
 
-def test_layer_tiny_config():
+def test_layer_tiny_config(path):
     c = synth.CONFIGS[1]
     lw, x, logits = _case(1, c.T, c.E, c.H, c.I, c.k)
     out = run_layer(lw, x, logits, c.k)
@@ -206,14 +213,14 @@ def test_layer_tiny_config():
 @pytest.mark.parametrize("T,E,H,I,k", [(37, 8, 576, 320, 4),     # >16 rows per expert, K tails
                                        (1, 16, 256, 128, 16),     # k = E, one token
                                        (64, 4, 256, 192, 4)])     # k = E, 64 rows per expert
-def test_layer_ragged_shapes(T, E, H, I, k):
+def test_layer_ragged_shapes(T, E, H, I, k, path):
     lw, x, logits = _case(21, T, E, H, I, k, e2m1_experts=(1,), permute="random")
     out = run_layer(lw, x, logits, k)
     ref = oracle.layer_forward(x, logits, k, lw)
     check_layer(out, ref, k)
 
 
-def test_layer_residual_in_place():
+def test_layer_residual_in_place(path):
     mq = _mq()
     T, E, H, I, k = 16, 4, 256, 128, 2
     lw, x, logits = _case(22, T, E, H, I, k)
@@ -228,7 +235,7 @@ def test_layer_residual_in_place():
     assert rel.max() < 5e-3
 
 
-def test_layer_invalid_expert_id_gives_nan_row():
+def test_layer_invalid_expert_id_gives_nan_row(path):
     mq = _mq()
     T, E, H, I, k = 4, 4, 256, 128, 2
     lw, x, logits = _case(23, T, E, H, I, k)
@@ -250,7 +257,7 @@ def test_layer_invalid_expert_id_gives_nan_row():
     assert rel.max() < ROW_REL_TOL
 
 
-def test_layer_invalid_table_id_gives_nan_rows():
+def test_layer_invalid_table_id_gives_nan_rows(path):
     T, E, H, I, k = 16, 4, 256, 128, 2
     lw, x, logits = _case(24, T, E, H, I, k)
     lw.table_id[2] = 7                       # only 2 tables exist
@@ -261,7 +268,7 @@ def test_layer_invalid_table_id_gives_nan_rows():
     assert uses2.any() and np.all(np.isnan(y[uses2])) and np.all(np.isfinite(y[~uses2]))
 
 
-def test_layer_deterministic():
+def test_layer_deterministic(path):
     T, E, H, I, k = 37, 8, 576, 320, 4
     lw, x, logits = _case(25, T, E, H, I, k)
     a = run_layer(lw, x, logits, k)
@@ -287,3 +294,70 @@ def test_glm_decode_t8_full(glm_layer):
     out = run_layer(glm_layer, x, logits, c.k)
     ref = oracle.layer_forward(x, logits, c.k, glm_layer)
     check_layer(out, ref, c.k)
+
+
+def _sample_tokens(ids, n, seed):
+    """n tokens: the ones routed to the most-loaded expert first, then random ones."""
+    counts = np.bincount(ids.ravel(), minlength=256)
+    hot = int(np.argmax(counts))
+    on_hot = np.where((ids == hot).any(1))[0]
+    g = np.random.default_rng(seed)
+    pick = list(g.choice(on_hot, size=min(2, len(on_hot)), replace=False))
+    rest = np.setdiff1d(np.arange(ids.shape[0]), pick)
+    pick += list(g.choice(rest, size=n - len(pick), replace=False))
+    return sorted(int(t) for t in pick)
+
+
+def test_glm_prefill_t2048_zipf_sampled():
+    c = synth.CONFIGS[3]
+    lw = synth.make_layer(3, c.E, c.H, c.I)
+    x = synth.make_x(3, c.T, c.H)
+    logits = synth.make_logits(3, c.T, c.E, zipf_s=c.zipf_s)
+    out = run_layer(lw, x, logits, c.k)
+    toks = _sample_tokens(out["ids"], 5, 3)
+    ref = oracle.layer_forward(x, logits, c.k, lw, tokens=toks)
+    check_layer(out, ref, c.k, tokens=toks)
+
+
+def test_glm_prefill_t8192_e2m1_permuted_sampled():
+    """8192 tokens, Zipf routing, the E2M1 experts of the model card's defect table and a
+    random intermediate-channel permutation baked into gate-N, up-N and down-K."""
+    c = synth.CONFIGS[5]
+    lw = synth.make_layer(5, c.E, c.H, c.I, e2m1_experts=c.e2m1, permute=c.permute)
+    x = synth.make_x(5, c.T, c.H)
+    logits = synth.make_logits(5, c.T, c.E, zipf_s=c.zipf_s)
+    out = run_layer(lw, x, logits, c.k)
+    ids = out["ids"]
+    toks = _sample_tokens(ids, 4, 5)
+    on_e2m1 = np.where(np.isin(ids, list(c.e2m1)).any(1))[0]
+    assert len(on_e2m1) > 0
+    toks = sorted(set(toks) | {int(on_e2m1[0])})
+    ref = oracle.layer_forward(x, logits, c.k, lw, tokens=toks)
+    check_layer(out, ref, c.k, tokens=toks)
+
+
+def test_block_permutation_relayout_gpu(path):
+    """A permutation that moves whole 32-channel blocks and channels within blocks can be
+    applied to the stored bytes exactly; outputs agree up to fp32 re-association. A changed
+    summation order can move an intermediate value across a bf16 rounding boundary: one such
+    flip changes y by about 2^-8 of that channel's share, hence a bound well above fp32
+    re-association (~1e-6) yet far below the parity bar."""
+    import copy
+    T, E, H, I, k = 64, 8, 512, 256, 4
+    lw, x, logits = _case(26, T, E, H, I, k)
+    g = np.random.default_rng(7)
+    perms = np.stack([np.concatenate([b * 32 + g.permutation(32) for b in g.permutation(I // 32)])
+                      for _ in range(E)])
+    q = copy.deepcopy(lw)
+    for e in range(E):
+        p = perms[e]
+        q.gate_codes[e], q.gate_scales[e] = lw.gate_codes[e][p], lw.gate_scales[e][p]
+        q.up_codes[e], q.up_scales[e] = lw.up_codes[e][p], lw.up_scales[e][p]
+        cd = oracle.unpack_codes(lw.down_codes[e])[:, p]
+        q.down_codes[e] = (cd[:, 0::2] | (cd[:, 1::2] << 4)).astype(np.uint8)
+        q.down_scales[e] = lw.down_scales[e][:, p[::32] // 32]
+    a = oracle.bf16_to_f64(run_layer(lw, x, logits, k)["y"])
+    b = oracle.bf16_to_f64(run_layer(q, x, logits, k)["y"])
+    rel = np.linalg.norm(a - b, axis=1) / np.linalg.norm(a, axis=1)
+    assert rel.max() < 1e-3
+    assert np.median(rel) < 1e-6
