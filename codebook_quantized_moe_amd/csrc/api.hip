@@ -124,8 +124,10 @@ extern "C" {
 const char* moeq_last_error(void) { return g_err; }
 
 size_t moeq_workspace_bytes(int T, int k, int E, int H, int I) {
-    (void)T; (void)k; (void)E; (void)H; (void)I;
-    return 0;
+    (void)k; (void)E; (void)I;
+    // the prefill gate|up path stages x in pair-split order
+    if (T <= 0 || H <= 0) return 0;
+    return prefill_split_bytes(T, H);
 }
 
 int moeq_route_topk(const float* logits, int T, int E, int k, int gating, int32_t* topk_ids,
@@ -171,6 +173,8 @@ static int projection(const char* w, bool gateup, const uint16_t* act, int T, in
     const size_t need = moeq_workspace_bytes(T, k, E, H, I);
     if (need > 0 && (!ws || ws_bytes < need))
         return fail(MOEQ_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", w, need, ws_bytes);
+    if (need > 0 && !aligned(ws, 16))
+        return fail(MOEQ_EUNSUPPORTED, "%s: the workspace must be 16-byte aligned", w);
     const long long act_bytes = gateup ? (long long)T * H * 2 : (long long)T * k * I * 2;
     const long long mat_bytes = gateup ? (long long)I * H / 2 : (long long)H * I / 2;
     if (act_bytes >= (1LL << 31) || mat_bytes >= (1LL << 31))
@@ -193,11 +197,17 @@ static int projection(const char* w, bool gateup, const uint16_t* act, int T, in
     a.N = gateup ? I : H;
     a.K = gateup ? H : I;
     a.out_ld = gateup ? I : H;
+
     const long touched = (long)(E < T * k ? E : T * k);
     clear_hip_error();
     if (use_prefill_path(T, k, E)) {
         // upper bound of the 128-row tiles the device will find
         const long tiles = touched + (long)T * k / prefill_tile_rows();
+        if (gateup) {
+            uint16_t* xs = static_cast<uint16_t*>(ws);
+            launch_pair_split_rows(static_cast<const uint16_t*>(act), T, H, xs, cu_count(), stream);
+            a.act = xs;
+        }
         launch_prefill(a, gateup, tiles, cu_count(), stream);
     } else {
         // upper bound of the 4-row tiles the device will find

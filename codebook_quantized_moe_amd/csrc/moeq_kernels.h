@@ -36,6 +36,9 @@ void launch_decode(const SkinnyArgs& a, bool gateup, long tiles, int cus, int sh
 int decode_tile_rows();
 void launch_prefill(const SkinnyArgs& a, bool gateup, long tiles, int cus, hipStream_t stream);
 int prefill_tile_rows();
+size_t prefill_split_bytes(int T, int H);
+void launch_pair_split_rows(const uint16_t* x, int T, int H, uint16_t* xs, int cus,
+                            hipStream_t stream);
 void launch_combine(const float* yp, const int32_t* pair_pos, const int32_t* offsets, int T, int k,
                     int E, int H, const uint16_t* residual, uint16_t* y, hipStream_t stream);
 void launch_dequant(const uint8_t* codes, const uint8_t* scales, int E, int N, int K,
