@@ -120,3 +120,17 @@ def test_last_error_is_cleared_on_success():
     assert mq.moeq_last_error() != ""
     mq.moeq_route_topk(None, 0, 256, 8, None, None, stream=0)
     assert mq.moeq_last_error() == ""
+
+
+def test_workspace_contract():
+    # T * H bf16 values (the pair-split copy of x), rounded up to 256 bytes; 0 for T = 0
+    assert mq.moeq_workspace_bytes(8, 8, 256, 6144, 2048) == 8 * 6144 * 2
+    assert mq.moeq_workspace_bytes(3, 8, 256, 64, 64) == 512
+    assert mq.moeq_workspace_bytes(0, 8, 256, 6144, 2048) == 0
+    need = mq.moeq_workspace_bytes(8, 8, 256, 6144, 2048)
+    assert _status(mq.moeq_gateup_swiglu, **_gateup()) == mq.MOEQ_EWORKSPACE
+    assert _status(mq.moeq_gateup_swiglu, **_gateup(ws=FAKE, ws_bytes=need - 1)) == \
+        mq.MOEQ_EWORKSPACE
+    assert _status(mq.moeq_gateup_swiglu, **_gateup(ws=FAKE + 8, ws_bytes=need)) == \
+        mq.MOEQ_EUNSUPPORTED
+    assert str(need) in mq.moeq_last_error() or "aligned" in mq.moeq_last_error()
