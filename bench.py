@@ -11,6 +11,8 @@ weights that the previous steps left in the ~256 MB last-level cache (MALL).
 Prints ONE JSON line. ``roofline`` covers the dominant kernel (the fused gate|up projection):
 algorithmic bytes (touched experts' gate+up codes and scales + activations in/out) per launch
 divided by its average launch time, measured with HIP events on the launch stream.
+``roofline.traffic`` is the kernel's HBM bytes per launch from the rocprofv3 counter summaries in
+``profiles/`` (null when none matches the current kernel source).
 ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -53,6 +55,36 @@ def parse():
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = {
+    "decode_kernel<true>": ["codebook_quantized_moe_amd/csrc/gemm_decode.hip",
+                            "codebook_quantized_moe_amd/csrc/moeq_device.h"],
+    "prefill_kernel<true>": ["codebook_quantized_moe_amd/csrc/gemm_prefill.hip",
+                             "codebook_quantized_moe_amd/csrc/moeq_device.h"],
+}
+
+
+def profiled_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the rocprofv3 counter summaries in
+    profiles/ (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, see there), or None when there is none or
+    the kernel's source has changed since the counters were taken (its hash is recorded)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    digest = h.hexdigest()[:16]
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as fh:
+            for line in fh:
+                if not line.startswith("traffic:"):
+                    continue
+                kv = dict(item.split("=", 1) for item in line.split()[1:])
+                if kv.get("kernel") == kernel and kv.get("workload") == workload:
+                    return int(kv["total_bytes"]) if kv.get("source_sha256") == digest else None
+    return None
 
 
 def cpu_baseline(cfg, lw, x, logits, n_tokens):
@@ -155,14 +187,18 @@ def main():
     ms_per_step = total_ms / args.steps
     value = T * args.steps / (total_ms / 1e3)
     gu_avg = float(np.mean(gu_ms))
+    kernel = "decode_kernel<true>" if decode else "prefill_kernel<true>"
+    traffic = profiled_traffic(kernel, cfg.name)
     if decode:
         ach = float(np.mean(gu_bytes)) / (gu_avg / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
     else:
         ach = flops_gu / (gu_avg / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+    roof["kernel"] = kernel
+    roof["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, profiles/)"
 
     out = {
         "metric": METRIC,
