@@ -102,7 +102,12 @@ int check_hk(const char* what, int H, int I) {
 // LDS once per tile) when experts get many rows on average, the decode kernels (4-row tiles,
 // weights decoded in registers, one pass over the weights) otherwise. MOEQ_FORCE_PATH=decode
 // or prefill overrides the choice (both are exact; used to test each on the same inputs).
+// The few-rows kernels keep one 4-byte entry per sorted row in LDS: they serve up to 4096
+// rows (every call with T * k < 16 E, as E <= 256); larger calls always take the other path.
+constexpr long long kDecodeMaxRows = 4096;
+
 bool use_prefill_path(int T, int k, int E) {
+    if ((long long)T * k > kDecodeMaxRows) return true;
     const char* f = getenv("MOEQ_FORCE_PATH");
     if (f && strcmp(f, "decode") == 0) return false;
     if (f && strcmp(f, "prefill") == 0) return true;
@@ -125,7 +130,7 @@ const char* moeq_last_error(void) { return g_err; }
 
 size_t moeq_workspace_bytes(int T, int k, int E, int H, int I) {
     (void)k; (void)E; (void)I;
-    // the prefill gate|up path stages x in pair-split order
+    // gate|up stages x in pair-split order
     if (T <= 0 || H <= 0) return 0;
     return prefill_split_bytes(T, H);
 }
@@ -200,14 +205,15 @@ static int projection(const char* w, bool gateup, const uint16_t* act, int T, in
 
     const long touched = (long)(E < T * k ? E : T * k);
     clear_hip_error();
+    if (gateup) {
+        // both projection families read x in the decoder's pair-split K order
+        uint16_t* xs = static_cast<uint16_t*>(ws);
+        launch_pair_split_rows(static_cast<const uint16_t*>(act), T, H, xs, cu_count(), stream);
+        a.act = xs;
+    }
     if (use_prefill_path(T, k, E)) {
         // upper bound of the 128-row tiles the device will find
         const long tiles = touched + (long)T * k / prefill_tile_rows();
-        if (gateup) {
-            uint16_t* xs = static_cast<uint16_t*>(ws);
-            launch_pair_split_rows(static_cast<const uint16_t*>(act), T, H, xs, cu_count(), stream);
-            a.act = xs;
-        }
         launch_prefill(a, gateup, tiles, cu_count(), stream);
     } else {
         // upper bound of the 4-row tiles the device will find

@@ -17,7 +17,7 @@
 //     staged per 2048-wide K-chunk by the whole workgroup with 16-byte loads, double-buffered
 //     (one barrier per chunk), and shared by its 8 wavefronts;
 //   * the exact bf16 decode tables (one 16-byte entry per table and scale byte).
-// Codes of the next PF K-steps stay in flight per wavefront, across chunk and item boundaries.
+// The codes of the next K-step stay in flight per wavefront, across chunk and item boundaries.
 //
 // Work item = (tile of <= 4 sorted rows of one expert, block of 64 channels for gate|up or
 // 128 output rows for down); a workgroup (8 wavefronts) takes one item at a time, wavefront w
@@ -49,10 +49,16 @@ struct DecShape {
     static constexpr int kChannelsPerWG = GATEUP_COLS(WAVES);   // gate|up channels per item
     static constexpr int kARowUnits = CHUNK / 8 + 1;              // 16-byte units per row (+1)
     static constexpr int kABufBytes = kTileRows * kARowUnits * 16;
-    static constexpr int kSBufBytes = kRowsPerWG * (CHUNK / 32);
+    // a weight row's CHUNK / 32 scale bytes, staged from the 16-byte boundary below them
+    static constexpr int kSRowBytes = CHUNK / 32 + 16;
+    static constexpr int kSBufBytes = kRowsPerWG * kSRowBytes;
 };
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// s_waitcnt until at most n vector-memory loads are outstanding (loads return in order)
+#define MOEQ_DEC_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 // non-temporal: the weight streams are read once (a plain read kernel reaches ~4.9 TB/s
 // with the default policy and ~6.8 TB/s with this hint on MI355X)
 constexpr int kStreamPolicy = 2;
@@ -77,17 +83,30 @@ __device__ __forceinline__ f32x4 mfma4x4x4(uint32_t a0, uint32_t a1, uint32_t b0
                                                   0, 0);
 }
 
-// Active experts (ascending) and the prefix count of their kTileRows-row tiles, in LDS.
-// Returns the count of active experts; tpre[count] is the number of tiles. All threads.
-__device__ inline int active_tiles(const int32_t* offsets, int E, int* active, int* tpre,
-                                   int* n_s) {
+// Per active expert (ascending ids), in LDS: its id, first sorted row, row count, decode
+// table id and the prefix count of its kTileRows-row tiles. Everything the K loop needs about
+// an item then comes from LDS: a vector-memory load inside the loop would have to wait for
+// every code load issued before it (loads return in order) and drain the prefetch.
+struct ExpertMeta {
+    int active[256];
+    int tpre[257];
+    int beg[256];
+    int cnt[256];
+    int tsel[256];
+    int n;
+};
+
+// Fills m (all threads call it; ends with a barrier). Returns the count of active experts.
+__device__ inline int active_tiles(const int32_t* offsets, const uint8_t* table_id, int E,
+                                   ExpertMeta& m) {
     const int lane = threadIdx.x & 63;
     if (threadIdx.x < 64) {
-        int rows[4], c = 0, nt = 0;
+        int rows[4], beg[4], c = 0, nt = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = lane * 4 + j;
-            rows[j] = e < E ? offsets[e + 1] - offsets[e] : 0;
+            beg[j] = e < E ? offsets[e] : 0;
+            rows[j] = e < E ? offsets[e + 1] - beg[j] : 0;
             c += rows[j] > 0;
             nt += (rows[j] + kTileRows - 1) / kTileRows;
         }
@@ -101,40 +120,45 @@ __device__ inline int active_tiles(const int32_t* offsets, int E, int* active, i
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             if (rows[j] > 0) {
-                active[pos] = lane * 4 + j;
-                tpre[pos] = pre;
+                const int e = lane * 4 + j;
+                m.active[pos] = e;
+                m.tpre[pos] = pre;
+                m.beg[pos] = beg[j];
+                m.cnt[pos] = rows[j];
+                m.tsel[pos] = table_id[e];
                 ++pos;
                 pre += (rows[j] + kTileRows - 1) / kTileRows;
             }
         if (lane == 63) {
-            *n_s = ic;
-            tpre[ic] = it;
+            m.n = ic;
+            m.tpre[ic] = it;
         }
     }
     __syncthreads();
-    return *n_s;
+    return m.n;
 }
 
 struct Item {
-    int e, cb, r0, rows;
+    int e, cb, r0, rows, tsel;
 };
 
-__device__ __forceinline__ Item locate(long item, int ncb, int nact, const int* active,
-                                       const int* tpre, const int32_t* offsets) {
+__device__ __forceinline__ Item locate(long item, int ncb, int nact, const ExpertMeta& m) {
     Item it;
     const int tile = (int)(item / ncb);
     it.cb = (int)(item % ncb);
-    int lo = 0, hi = nact - 1;                    // last a with tpre[a] <= tile
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tpre[mid] <= tile) lo = mid; else hi = mid - 1;
+    // last a < nact with tpre[a] <= tile: a fixed, unrolled search (no loop in the K loop)
+    int lo = 0;
+#pragma unroll
+    for (int step = 128; step >= 1; step >>= 1) {
+        const int c = lo + step;
+        if (c < nact && m.tpre[c] <= tile) lo = c;
     }
-    it.e = __builtin_amdgcn_readfirstlane(active[lo]);
-    const int m0 = (tile - __builtin_amdgcn_readfirstlane(tpre[lo])) * kTileRows;
-    const int beg = __builtin_amdgcn_readfirstlane(offsets[it.e]);
-    const int end = __builtin_amdgcn_readfirstlane(offsets[it.e + 1]);
-    it.r0 = beg + m0;
-    it.rows = min(kTileRows, end - it.r0);
+    lo = __builtin_amdgcn_readfirstlane(lo);
+    it.e = __builtin_amdgcn_readfirstlane(m.active[lo]);
+    const int m0 = (tile - __builtin_amdgcn_readfirstlane(m.tpre[lo])) * kTileRows;
+    it.r0 = __builtin_amdgcn_readfirstlane(m.beg[lo]) + m0;
+    it.rows = min(kTileRows, __builtin_amdgcn_readfirstlane(m.cnt[lo]) - m0);
+    it.tsel = __builtin_amdgcn_readfirstlane(m.tsel[lo]);
     return it;
 }
 
@@ -149,21 +173,28 @@ __device__ __forceinline__ int weight_row(int cb, int w, int g, int q, int* mat)
     return cb * S::kRowsPerWG + w * 16 + g * 4 + q;
 }
 
-template <bool GATEUP, int PF, class S>
+template <bool GATEUP, class S>
 __global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 decode_kernel(const SkinnyArgs a) {
     constexpr int kChunkK = S::kChunkK, kRowsPerWG = S::kRowsPerWG;
     constexpr int kARowUnits = S::kARowUnits, kABufBytes = S::kABufBytes;
-    constexpr int kSBufBytes = S::kSBufBytes;
+    constexpr int kSBufBytes = S::kSBufBytes, kSRowBytes = S::kSRowBytes;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    __shared__ int active[256];
-    __shared__ int tpre[257];
-    __shared__ int n_active_s;
+    __shared__ ExpertMeta meta;
     u32x4* tab = reinterpret_cast<u32x4*>(smem);
     uint8_t* abuf = smem + (size_t)a.tables.n * 256 * 16;
     uint8_t* sbuf = abuf + 2 * kABufBytes;
+    // per sorted row: gate|up the token (x row), down the gate weight topk_w[pair]
+    uint8_t* rowinfo = sbuf + 2 * kSBufBytes;
+    uint16_t* row_tok = reinterpret_cast<uint16_t*>(rowinfo);
+    float* row_w = reinterpret_cast<float*>(rowinfo);
     build_decode_tables(a.tables, tab);
-    const int nact = active_tiles(a.offsets, a.E, active, tpre, &n_active_s);
+    for (int r = threadIdx.x; r < a.T * a.k; r += blockDim.x) {
+        const int p = a.sorted_pair[r];
+        if (GATEUP) row_tok[r] = (uint16_t)(p / a.k);
+        else row_w[r] = a.topk_w[p];
+    }
+    const int nact = active_tiles(a.offsets, a.table_id, a.E, meta);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -171,8 +202,10 @@ decode_kernel(const SkinnyArgs a) {
     const int K = a.K, N = a.N;
     const int ncb = GATEUP ? (N + S::kChannelsPerWG - 1) / S::kChannelsPerWG
                            : (N + kRowsPerWG - 1) / kRowsPerWG;
-    const long items = (long)__builtin_amdgcn_readfirstlane(tpre[nact]) * ncb;
-    const int nsteps = (K + kStepK - 1) / kStepK;
+    const long items = (long)__builtin_amdgcn_readfirstlane(meta.tpre[nact]) * ncb;
+    // whole chunks of K-steps (steps past K load nothing in range and add zeros), so that
+    // every chunk issues the same number of code loads after its staging DMA
+    const int nsteps = (K + kChunkK - 1) / kChunkK * (kChunkK / kStepK);
     const long first = blockIdx.x, stride = gridDim.x;
     const long nmine = items > first ? (items - first + stride - 1) / stride : 0;
     const long total = nmine * nsteps;
@@ -181,286 +214,242 @@ decode_kernel(const SkinnyArgs a) {
     const uint32_t mc = (uint32_t)N * kb, ms = (uint32_t)N * ks;
     const __amdgpu_buffer_rsrc_t ract = make_rsrc(a.act, a.act_bytes);
 
-    // ---------------- code stream (per wavefront, PF K-steps ahead) ----------------
-    struct CodeSrc {
-        __amdgpu_buffer_rsrc_t r0, r1;           // gate (or down) and up codes of the expert
-        uint32_t off[4];                         // byte offset of this lane's row, per group
+    // ---------------- one item's sources ----------------
+    // Items past the end (the "next" of the last item) are empty: every load falls out of
+    // range and returns zeros, so the loop below needs no branches around its loads.
+    struct Src {
+        __amdgpu_buffer_rsrc_t c0, c1;            // gate (or down) and up codes of the expert
+        uint32_t off[4];                          // this lane's code row per group (or none)
+        int e, cb, r0, rows, tsel;
     };
-    auto code_src = [&](long item) {
-        const Item it = locate(item, ncb, nact, active, tpre, a.offsets);
-        CodeSrc s;
-        s.r0 = make_rsrc(a.codes0 + (size_t)it.e * mc, mc);
-        s.r1 = GATEUP ? make_rsrc(a.codes1 + (size_t)it.e * mc, mc) : s.r0;
+    auto make_src = [&](long item) {
+        Src sr;
+        const bool valid = item < items;
+        const Item it = locate(valid ? item : first, ncb, nact, meta);
+        sr.e = it.e;
+        sr.cb = it.cb;
+        sr.r0 = it.r0;
+        sr.rows = valid ? it.rows : 0;
+        sr.tsel = it.tsel;
+        sr.c0 = make_rsrc(a.codes0 + (size_t)it.e * mc, mc);
+        sr.c1 = GATEUP ? make_rsrc(a.codes1 + (size_t)it.e * mc, mc) : sr.c0;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             int mat;
             const int row = weight_row<GATEUP, S>(it.cb, wave, g, q, &mat);
-            s.off[g] = row < N ? (uint32_t)row * kb + (uint32_t)b * 16 : kOutOfRange;
+            sr.off[g] = (valid && row < N) ? (uint32_t)row * kb + (uint32_t)b * 16 : kOutOfRange;
         }
-        return s;
+        return sr;
     };
-    long l_item = first;
-    int l_step = 0;
-    CodeSrc lsrc = code_src(l_item);
-    auto load_codes = [&]() {
-        const int kk = l_step * kStepK;
-        const bool ok = l_item < items && kk + b * 32 < K;
-        u32x4 c[4];
+    // codes of K-step st: lane (b, q) of group g reads 32 codes of row 4 g + q at K 32 b
+    auto load_step = [&](const Src& sr, int st, u32x4 (&c)[4]) {
+        const int kk = st * kStepK;
+        const bool ok = kk + b * 32 < K;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const uint32_t off = (ok && lsrc.off[g] != kOutOfRange) ? lsrc.off[g] + kk / 2
-                                                                     : kOutOfRange;
-            c[g] = bload16<kStreamPolicy>((GATEUP && g >= 2) ? lsrc.r1 : lsrc.r0, off);
+            const uint32_t off = (ok && sr.off[g] != kOutOfRange) ? sr.off[g] + kk / 2 : kOutOfRange;
+            c[g] = bload16<kStreamPolicy>((GATEUP && g >= 2) ? sr.c1 : sr.c0, off);
         }
-        if (++l_step == nsteps) {
-            l_step = 0;
-            l_item += stride;
-            if (l_item < items) lsrc = code_src(l_item);
-        }
-        struct R { u32x4 c[4]; } r;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) r.c[g] = c[g];
-        return r;
     };
 
     // ---------------- staging of activations and scales (per workgroup, per chunk) -------
-    // staging: activations are kTileRows rows x (kChunkK / 8) 16-byte pieces, scales are
-    // kRowsPerWG rows x (kChunkK / 512) 16-byte pieces
-    constexpr int kAPieces = kTileRows * (kChunkK / 8);
-    constexpr int kAPerThread = kAPieces / S::kThreads;
-    constexpr int kSPiecesPerRow = kChunkK / 512;
-    static_assert(kAPieces % S::kThreads == 0, "activation staging");
-    static_assert(kRowsPerWG * kSPiecesPerRow <= S::kThreads, "scale staging: <= 1 piece per thread");
-    const bool s_thread = tid < kRowsPerWG * kSPiecesPerRow;
-    struct Stage {
-        u32x4 x[kAPerThread];
-        u32x4 s;
-    };
-    const int ss_row = tid / kSPiecesPerRow, ss_p = tid % kSPiecesPerRow;
-    auto stage_load = [&](long item, int chunk) {
-        Stage st;
-        const Item it = locate(item, ncb, nact, active, tpre, a.offsets);
+    // Both go global -> LDS by LDS-DMA (16 bytes per lane, lane-contiguous), issued at the
+    // start of the chunk before and waited for at its end:
+    //   * activations: kTileRows rows x kARowUnits 16-byte units (the last unit of a row is
+    //     padding, so that the 4 rows of an MFMA operand read sit in different banks);
+    //     the rows are already in pair-split K order (x is split once per call, the
+    //     intermediate is stored that way);
+    //   * scales: row R of the item (gate|up: R = 64 mat + channel, so gate rows and up rows
+    //     fill separate DMA loads) gets kSRowBytes bytes from the 16-byte boundary at or
+    //     below its first scale byte of the chunk; readers add the row's offset (row * K/32
+    //     mod 16). Bytes past a row's K are masked at read time.
+    constexpr int kAUnits = kTileRows * kARowUnits;
+    constexpr int kALoads = (kAUnits + 63) / 64;
+    constexpr int kSLoads = kSBufBytes / 1024;
+    constexpr int kSUnitsPerRow = kSRowBytes / 16;
+    static_assert(kSBufBytes % 1024 == 0 && (kRowsPerWG / 2) * kSRowBytes % 1024 == 0,
+                  "scale staging: whole DMA loads, gate and up rows in separate loads");
+    auto stage_dma = [&](const Src& sr, int chunk, int sbufi) {
         const int kc = chunk * kChunkK;
-        // activations: piece i = tid + j * threads -> tile row i / (kChunkK / 8), elements
-        // kc + 8 (i % (kChunkK / 8)) .. + 7
-#pragma unroll
-        for (int j = 0; j < kAPerThread; ++j) {
-            const int i = tid + j * S::kThreads;
-            const int row = i / (kChunkK / 8), k0 = kc + (i % (kChunkK / 8)) * 8;
-            uint32_t off = kOutOfRange;
-            if (row < it.rows && k0 < K) {
-                const uint32_t src = GATEUP ? (uint32_t)(a.sorted_pair[it.r0 + row] / a.k)
-                                            : (uint32_t)(it.r0 + row);
-                off = (src * (uint32_t)K + (uint32_t)k0) * 2u;
-            }
-            st.x[j] = bload16<0>(ract, off);
-        }
-        // scales: weight row ss_row of the item, bytes kc/32 + 16 p .. + 15
-        const int w = ss_row >> 4, g = (ss_row >> 2) & 3, qq = ss_row & 3;
-        int mat;
-        const int row = weight_row<GATEUP, S>(it.cb, w, g, qq, &mat);
-        const int sb = kc / 32 + ss_p * 16;                  // first scale byte of the piece
-        const int valid = min(16, (int)ks - sb);             // bytes of this row in range
-        u32x4 sv = {0, 0, 0, 0};
-        if (s_thread && row < N && valid > 0) {
-            const uint8_t* sbase = (mat ? a.scales1 : a.scales0) + (size_t)it.e * ms;
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(sbase, ms);
-            // a row of K/32 scale bytes is only 2-byte aligned in general: load the dwords
-            // around it from the 4-byte boundary below and shift the bytes into place
-            const uint32_t off = (uint32_t)row * ks + (uint32_t)sb;
-            const u32x4 lo = bload16<kStreamPolicy>(rs, off & ~3u);
-            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(rs, (off & ~3u) + 16, 0,
-                                                                    kStreamPolicy);
-            const uint32_t sh = off & 3u;
-            sv = u32x4{__builtin_amdgcn_alignbyte(lo[1], lo[0], sh),
-                       __builtin_amdgcn_alignbyte(lo[2], lo[1], sh),
-                       __builtin_amdgcn_alignbyte(lo[3], lo[2], sh),
-                       __builtin_amdgcn_alignbyte(hi, lo[3], sh)};
-            // bytes past the row's end belong to the next row: clear them (K tail)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int nb = valid - 4 * j;
-                if (nb <= 0) sv[j] = 0;
-                else if (nb < 4) sv[j] &= (1u << (8 * nb)) - 1u;
+        uint8_t* ab = abuf + sbufi * kABufBytes;
+        uint8_t* sbb = sbuf + sbufi * kSBufBytes;
+        for (int i = wave; i < kALoads + kSLoads; i += S::kWaves) {
+            if (i < kALoads) {
+                const int u = i * 64 + lane;
+                const int row = u / kARowUnits, p = u % kARowUnits;
+                uint32_t off = kOutOfRange;
+                if (row < sr.rows && p < kChunkK / 8 && kc + 8 * p < K) {
+                    const uint32_t src = GATEUP ? (uint32_t)row_tok[sr.r0 + row]
+                                                : (uint32_t)(sr.r0 + row);
+                    off = (src * (uint32_t)K + (uint32_t)(kc + 8 * p)) * 2u;
+                }
+                if (u < kAUnits)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(ract, ab + i * 1024, 16, off, 0, 0, 0);
+            } else {
+                const int j = i - kALoads;
+                const int u = j * 64 + lane;
+                const int R = u / kSUnitsPerRow, piece = u % kSUnitsPerRow;
+                int wrow, mat;
+                if (GATEUP) {
+                    mat = R / (kRowsPerWG / 2);
+                    wrow = sr.cb * S::kChannelsPerWG + R % (kRowsPerWG / 2);
+                } else {
+                    mat = 0;
+                    wrow = sr.cb * kRowsPerWG + R;
+                }
+                const uint8_t* sbase = (mat ? a.scales1 : a.scales0) + (size_t)sr.e * ms;
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(sbase, ms);
+                const uint32_t first_b = (uint32_t)wrow * ks + (uint32_t)(kc / 32);
+                const uint32_t off = (sr.rows > 0 && wrow < N)
+                                         ? (first_b & ~15u) + 16u * (uint32_t)piece : kOutOfRange;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, sbb + j * 1024, 16, off, 0, 0,
+                                                         kStreamPolicy);
             }
         }
-        st.s = sv;
-        return st;
-    };
-    auto stage_store = [&](const Stage& st, int buf) {
-#pragma unroll
-        for (int j = 0; j < kAPerThread; ++j) {
-            const int i = tid + j * S::kThreads;
-            const int row = i / (kChunkK / 8), p = i % (kChunkK / 8);
-            const u32x4 x = GATEUP ? pair_split(st.x[j]) : st.x[j];   // x arrives natural
-            *reinterpret_cast<u32x4*>(abuf + buf * kABufBytes + (row * kARowUnits + p) * 16) = x;
-        }
-        if (s_thread)
-            *reinterpret_cast<u32x4*>(sbuf + buf * kSBufBytes + ss_row * (kChunkK / 32) +
-                                      ss_p * 16) = st.s;
     };
 
-    // first chunk of the first item, synchronously
-    const int nchunks = (K + kChunkK - 1) / kChunkK;
-    {
-        const Stage st = stage_load(first, 0);
-        stage_store(st, 0);
-    }
+    // ---------------- main loop ----------------
+    // Per chunk of kSteps K-steps: the next chunk (of this item or the next one) is staged by
+    // DMA into the other buffers; the codes of each K-step were loaded one K-step ahead into
+    // one of two register slots (cA for even steps, cB for odd ones); after the chunk the DMA
+    // is waited for (the 4 kSteps code loads issued after it may stay in flight) and one
+    // barrier switches the buffers.
+    constexpr int kSteps = kChunkK / kStepK;
+    static_assert(kSteps % 2 == 0, "even K-steps per chunk");
+    const int nchunks = nsteps / kSteps;
+    Src cur = make_src(first);
+    Src nxt = make_src(first + stride);
+    stage_dma(cur, 0, 0);
+    MOEQ_DEC_WAIT_VMCNT(0);
     __syncthreads();
+    u32x4 cA[4], cB[4];
+    load_step(cur, 0, cA);
+    int buf = 0;
 
-    struct Ring { u32x4 c[4]; };
-    Ring ring[PF + 1];
+    for (long n = 0; n < nmine; ++n) {
+        const bool badtab = cur.tsel >= a.tables.n;
+        const u32x4* mytab = tab + (badtab ? 0 : cur.tsel) * 256;
+        int soff[4];
+        f32x4 acc[4];
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-        auto r = load_codes();
-#pragma unroll
-        for (int g = 0; g < 4; ++g) ring[u].c[g] = r.c[g];
-    }
-
-    // staging cursor: the chunk after the one being computed
-    long s_item = first;
-    int s_chunk = 0;
-    auto advance_chunk = [&](long& item, int& chunk) {
-        if (++chunk == nchunks) { chunk = 0; item += stride; }
-    };
-    advance_chunk(s_item, s_chunk);
-    int buf = 0;                                  // buffer of the chunk being computed
-    Stage pending;
-
-    Item cp;
-    const u32x4* mytab = tab;
-    bool badtab = false;
-    f32x4 acc[4];
-    long c_item = first;
-    int c_step = 0;
-
-    for (long q0 = 0; q0 < total; q0 += PF + 1) {
-#pragma unroll
-        for (int u = 0; u < PF + 1; ++u) {
-            if (q0 + u >= total) break;
-            if (c_step == 0) {
-                cp = locate(c_item, ncb, nact, active, tpre, a.offsets);
-                const int tsel = a.table_id[cp.e];
-                badtab = tsel >= a.tables.n;
-                mytab = tab + (badtab ? 0 : tsel) * 256;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-            const int kk = c_step * kStepK;
-            const int sub = (kk % kChunkK) / kStepK;
-            const int chunk_end = min(nsteps, (kk / kChunkK + 1) * (kChunkK / kStepK));
-            const bool last_in_chunk = c_step + 1 == chunk_end;
-            const bool more = s_item < first + nmine * stride;   // a next chunk exists
-            if (sub == 0 && more) pending = stage_load(s_item, s_chunk);
-            {
-                auto r = load_codes();
-#pragma unroll
-                for (int g = 0; g < 4; ++g) ring[(u + PF) % (PF + 1)].c[g] = r.c[g];
-            }
-            const Ring& cur = ring[u];
+        for (int g = 0; g < 4; ++g) {
+            int mat;
+            const int wrow = weight_row<GATEUP, S>(cur.cb, wave, g, q, &mat);
+            const int R = GATEUP ? mat * (kRowsPerWG / 2) + (wrow - cur.cb * S::kChannelsPerWG)
+                                 : wrow - cur.cb * kRowsPerWG;
+            soff[g] = R * kSRowBytes + (int)(((uint32_t)wrow * ks) & 15u);
+            acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        auto compute = [&](const u32x4 (&c)[4], int kk) {
             // activation operands: tile row q, K 32 b .. 32 b + 31 of the step (pair-split)
             const uint8_t* ap = abuf + buf * kABufBytes + q * kARowUnits * 16 +
                                 ((kk % kChunkK) / 8 + b * 4) * 16;
             u32x4 A[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) A[j] = *reinterpret_cast<const u32x4*>(ap + 16 * j);
-            const uint8_t* sp = sbuf + buf * kSBufBytes + (wave * 16 + q) * (kChunkK / 32) +
-                                (kk % kChunkK) / 32 + b;
+            const uint8_t* sp = sbuf + buf * kSBufBytes + (kk % kChunkK) / 32 + b;
+            const bool kin = kk + 32 * b < K;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const uint32_t s = sp[g * 4 * (kChunkK / 32)];
-                const u32x4 t = mytab[s];
+                const uint32_t sc = kin ? (uint32_t)sp[soff[g]] : 0u;
+                const u32x4 t = mytab[sc];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const u32x4 w = decode8(cur.c[g][j], t);
+                    const u32x4 w = decode8(c[g][j], t);
                     acc[g] = mfma4x4x4(A[j][0], A[j][1], w[0], w[1], acc[g]);
                     acc[g] = mfma4x4x4(A[j][2], A[j][3], w[2], w[3], acc[g]);
                 }
             }
-            if (last_in_chunk) {
-                if (more) {
-                    stage_store(pending, buf ^ 1);
-                    advance_chunk(s_item, s_chunk);
-                }
-                __syncthreads();
-                buf ^= 1;
+        };
+        for (int ch = 0; ch < nchunks; ++ch) {
+            const bool lastc = ch + 1 == nchunks;
+            const Src& ns = lastc ? nxt : cur;     // source of the next chunk
+            stage_dma(ns, lastc ? 0 : ch + 1, buf ^ 1);
+#pragma unroll
+            for (int j = 0; j < kSteps; ++j) {
+                const int st = ch * kSteps + j;
+                if (j + 1 < kSteps) load_step(cur, st + 1, (j & 1) ? cA : cB);
+                else load_step(ns, lastc ? 0 : st + 1, (j & 1) ? cA : cB);
+                compute((j & 1) ? cB : cA, st * kStepK);
             }
-            if (++c_step < nsteps) continue;
-            // ---- item complete: sum the 16 K-slices (lanes q, q + 4, ..., q + 60) ----
-            c_step = 0;
-            c_item += stride;
+            MOEQ_DEC_WAIT_VMCNT(4 * kSteps);
+            __syncthreads();
+            buf ^= 1;
+        }
+
+        // ---- item complete: sum the 16 K-slices (lanes q, q + 4, ..., q + 60) ----
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = acc[g][r];
-                    v += __shfl_xor(v, 4, 64);
-                    v += __shfl_xor(v, 8, 64);
-                    v += __shfl_xor(v, 16, 64);
-                    v += __shfl_xor(v, 32, 64);
-                    acc[g][r] = v;
-                }
-            if (lane >= 4) continue;
+            for (int r = 0; r < 4; ++r) {
+                float v = acc[g][r];
+                v += __shfl_xor(v, 4, 64);
+                v += __shfl_xor(v, 8, 64);
+                v += __shfl_xor(v, 16, 64);
+                v += __shfl_xor(v, 32, 64);
+                acc[g][r] = v;
+            }
+        if (lane < 4) {
             // lane q holds rows 0..3 of this wavefront's columns 4 g + q
             if (GATEUP) {
                 uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const int ch = cp.cb * S::kChannelsPerWG + wave * 8 + h * 4 + q;
+                    const int ch = cur.cb * S::kChannelsPerWG + wave * 8 + h * 4 + q;
                     if (ch >= N) continue;
                     const int slot = (ch & ~7) | (((ch & 1) << 2) | ((ch & 7) >> 1));
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        if (r >= cp.rows) continue;
+                        if (r >= cur.rows) continue;
                         const float v = badtab ? __builtin_nanf("")
                                                : silu_mul(acc[h][r], acc[2 + h][r]);
-                        out[(size_t)(cp.r0 + r) * a.out_ld + slot] = (uint16_t)f32_to_bf16_rne(v);
+                        out[(size_t)(cur.r0 + r) * a.out_ld + slot] = (uint16_t)f32_to_bf16_rne(v);
                     }
                 }
             } else {
                 float* out = reinterpret_cast<float*>(a.out);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    if (r >= cp.rows) continue;
-                    const size_t row = (size_t)(cp.r0 + r);
-                    const float wgt = a.topk_w[a.sorted_pair[row]];
+                    if (r >= cur.rows) continue;
+                    const size_t row = (size_t)(cur.r0 + r);
+                    const float wgt = row_w[row];
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const int col = cp.cb * kRowsPerWG + wave * 16 + g * 4 + q;
+                        const int col = cur.cb * kRowsPerWG + wave * 16 + g * 4 + q;
                         if (col >= N) continue;
                         out[row * a.out_ld + col] = badtab ? __builtin_nanf("") : wgt * acc[g][r];
                     }
                 }
             }
         }
+        cur = nxt;
+        nxt = make_src(first + (n + 2) * stride);
     }
 }
 
 template <class S>
 static void launch_shape(const SkinnyArgs& a, bool gateup, long items, int cus, hipStream_t stream) {
-    const size_t lds = (size_t)a.tables.n * 256 * 16 + 2 * S::kABufBytes + 2 * S::kSBufBytes;
-    constexpr int PF = 2;
+    const size_t lds = (size_t)a.tables.n * 256 * 16 + 2 * S::kABufBytes + 2 * S::kSBufBytes +
+                       (size_t)a.T * a.k * (gateup ? 2 : 4);
     const int per_cu = 16 / S::kWaves;                    // 4 wavefronts per SIMD
     const long blocks = std::max(1L, std::min(items, (long)cus * per_cu));
     if (gateup)
-        hipLaunchKernelGGL((decode_kernel<true, PF, S>), dim3(blocks), dim3(S::kThreads), lds,
+        hipLaunchKernelGGL((decode_kernel<true, S>), dim3(blocks), dim3(S::kThreads), lds,
                            stream, a);
     else
-        hipLaunchKernelGGL((decode_kernel<false, PF, S>), dim3(blocks), dim3(S::kThreads), lds,
+        hipLaunchKernelGGL((decode_kernel<false, S>), dim3(blocks), dim3(S::kThreads), lds,
                            stream, a);
 }
 
 int decode_tile_rows() { return kTileRows; }
 
-// shape 0: 8 wavefronts, 2048-wide chunks; 1: 4 wavefronts, 2048; 2: 8 wavefronts, 1024;
-// 3: 4 wavefronts, 1024; 4: 16 wavefronts, 2048
+// shape 0: 8 wavefronts, 2048-wide chunks; 2: 8 wavefronts, 1024; 4: 16 wavefronts, 2048
+// (tuning alternatives; any other value selects shape 0)
 void launch_decode(const SkinnyArgs& a, bool gateup, long tiles, int cus, int shape,
                    hipStream_t stream) {
     auto items = [&](int cols) { return tiles * ((a.N + cols - 1) / cols); };
     switch (shape) {
-    case 1: launch_shape<DecShape<4, 2048>>(a, gateup, items(gateup ? 32 : 64), cus, stream); break;
     case 2: launch_shape<DecShape<8, 1024>>(a, gateup, items(gateup ? 64 : 128), cus, stream); break;
-    case 3: launch_shape<DecShape<4, 1024>>(a, gateup, items(gateup ? 32 : 64), cus, stream); break;
     case 4: launch_shape<DecShape<16, 2048>>(a, gateup, items(gateup ? 128 : 256), cus, stream); break;
     default: launch_shape<DecShape<8, 2048>>(a, gateup, items(gateup ? 64 : 128), cus, stream); break;
     }

@@ -72,9 +72,9 @@ static inline int moeq_inter_slot(int c) {
 const char* moeq_last_error(void);
 
 /* Bytes of device workspace that moeq_gateup_swiglu and moeq_down need for these sizes
- * (0 means they accept ws = NULL). Currently T * H * 2 rounded up to 256: the many-token
- * gate|up path first writes a copy of x with every 8-element group in the pair-split order
- * of moeq_inter_slot into it. The workspace must be 16-byte aligned; its contents are scratch
+ * (0 means they accept ws = NULL). Currently T * H * 2 rounded up to 256: gate|up first
+ * writes a copy of x with every 8-element group in the pair-split order of moeq_inter_slot
+ * into it. The workspace must be 16-byte aligned; its contents are scratch
  * between calls (two calls that run at the same time need two workspaces). */
 size_t moeq_workspace_bytes(int T, int k, int E, int H, int I);
 
