@@ -229,7 +229,8 @@ class LayerWeights:
 
 
 def make_layer(cfg_id: int, E: int, H: int, I: int, layer: int = 0, e2m1_experts=(),
-               permute: str | None = None, experts=None) -> LayerWeights:
+               permute: str | None = None, experts=None,
+               sigma: float = WEIGHT_SIGMA) -> LayerWeights:
     """Encode a layer's experts.
 
     permute: None, "random" (a random permutation of the I intermediate channels per expert)
@@ -237,6 +238,7 @@ def make_layer(cfg_id: int, E: int, H: int, I: int, layer: int = 0, e2m1_experts
     gate/up row n and the stored down column n hold logical channel perms[e, n]; the logical
     (unpermuted) weights are the draws at the logical indices.
     experts: optional subset of expert ids to encode (others left as zero bytes).
+    sigma: standard deviation of the N(0, sigma) weights before encoding.
     """
     grid = lloyd_grid(cfg_id, layer)
     tables = np.stack([grid, E2M1_GRID]).astype(np.float32)
@@ -268,11 +270,11 @@ def make_layer(cfg_id: int, E: int, H: int, I: int, layer: int = 0, e2m1_experts
         tab = tables[table_id[e]]
         rs = None if perms is None else perms[e]
         rtn_normal_into(key(cfg_id, S_WEIGHTS, layer, e, 0), I, H, tab, gate_codes[e],
-                        gate_scales[e], row_src=rs)
+                        gate_scales[e], row_src=rs, sigma=sigma)
         rtn_normal_into(key(cfg_id, S_WEIGHTS, layer, e, 1), I, H, tab, up_codes[e],
-                        up_scales[e], row_src=rs)
+                        up_scales[e], row_src=rs, sigma=sigma)
         rtn_normal_into(key(cfg_id, S_WEIGHTS, layer, e, 2), H, I, tab, down_codes[e],
-                        down_scales[e], col_src=rs)
+                        down_scales[e], col_src=rs, sigma=sigma)
     return LayerWeights(gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales,
                         tables, table_id, perms,
                         dict(cfg=cfg_id, layer=layer, E=E, H=H, I=I, permute=permute))
@@ -296,14 +298,19 @@ class Config:
     e2m1: tuple = ()
     permute: str | None = None
     residual: bool = False
+    sigma: float = WEIGHT_SIGMA
 
 
 CONFIGS = {
     1: Config(1, "tiny", H=256, I=128, E=4, k=2, T=16),
     2: Config(2, "glm_decode_t8", H=6144, I=2048, E=256, k=8, T=8),
     3: Config(3, "glm_prefill_t2048_zipf", H=6144, I=2048, E=256, k=8, T=2048, zipf_s=1.0),
+    # The stack's weight scale is not given; with N(0, 0.02) and no normalisation between
+    # layers the residual stream grows about quadratically per layer (SwiGLU is quadratic in
+    # its input) and overflows bf16 within ~10 layers. N(0, 0.01) keeps it bounded (rms
+    # ~1.1 after 32 layers in a dense fp32 simulation).
     4: Config(4, "glm_stack32_decode_t64", H=6144, I=2048, E=256, k=8, T=64, layers=32,
-              residual=True),
+              residual=True, sigma=0.01),
     5: Config(5, "glm_prefill_t8192_zipf_e2m1_perm", H=6144, I=2048, E=256, k=8, T=8192,
               zipf_s=1.0, e2m1=E2M1_DEFECT_EXPERTS, permute="random"),
 }
