@@ -61,7 +61,8 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     # plain host link (no implicit -lamdhip64): the device code objects are embedded in the
     # host objects and registered by their constructors
-    _run([CLANGXX, "-shared", "-fPIC", *objs, "-o", tmp,
+    # --no-undefined: a kernel whose host stub is missing fails here, not at load time
+    _run([CLANGXX, "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp,
           os.path.join(rt, "libamdhip64.so"), f"-Wl,-rpath,{rt}"], verbose)
     os.replace(tmp, LIB)
     return LIB

@@ -1,29 +1,32 @@
 // Grouped projections for many rows per expert (prefill): the MFMA work dominates.
 //
-// Tile. A workgroup of 4 wavefronts computes 128 sorted rows of one expert against 256 weight
-// rows over the whole K, in stages of 64 along K, with v_mfma_f32_32x32x16_bf16 (fp32
-// accumulation). Every wavefront owns 64 weight rows (two 32-column MFMA tiles) across all
-// 128 rows (four 32-row MFMA tiles), so the weights a wavefront needs are its own:
-//   * weights go global -> registers -> decoded in registers -> MFMA B operand. A lane holds
-//     one weight row and one 32-wide half of the stage's K, i.e. 16 code bytes and exactly one
-//     E8M0 scale byte per stage (one decode-table lookup for 32 weights). The code and scale
-//     loads run two stages ahead in a ring of three register sets.
-//   * activations are shared by the four wavefronts and go through LDS: each stage the
-//     workgroup loads the 128 x 64 bf16 tile (x rows through sorted_pair for gate|up, the
-//     intermediate's rows for down; both already in the pair-split K order of the decoder)
-//     one stage ahead into registers and stores it into the other half of a double-buffered
-//     LDS tile; one barrier closes the stage. LDS rows are 128 bytes with their 16-byte units
-//     XOR-swizzled by (r1, r0 ^ r2, r0 ^ r3), so that the MFMA operand reads (16 consecutive
-//     rows, one unit) and the staging writes cover all 64 banks.
-// The MFMA K index is mapped so that lane half h of kq-step q holds stage K 32 h + 8 q + (the
-// pair-split order of 0..7): the B lane's 32 weights are one contiguous, single-scale block,
-// and the A operand reads unit 4 h + q of its row.
+// Tile. A workgroup of 8 wavefronts (one workgroup per CU, two wavefronts per SIMD) computes
+// 128 sorted rows of one expert against 512 weight rows over the whole K, in stages of 64
+// along K, with v_mfma_f32_32x32x16_bf16 (fp32 accumulation). Every wavefront owns 64 weight
+// rows (two 32-column MFMA tiles) across all 128 rows (four 32-row MFMA tiles).
+//   * Both operands are staged in LDS by LDS-DMA (buffer loads that write LDS directly), so
+//     that every global request is a whole 64-byte sector: the 128 x 64 bf16 activation tile
+//     of a stage (x rows through sorted_pair for gate|up, the intermediate's rows for down;
+//     both already in the pair-split K order of the decoder) three stages ahead, and the code
+//     bytes of the 512 weight rows for a super-stage of S stages (S = 2: 64 bytes a row) about
+//     two stages ahead. The workgroup thus fetches each activation and code byte once per
+//     item, and a CU keeps more data per request in flight than with per-lane register loads.
+//   * A lane holds one weight row and one 32-wide half of the stage's K: 16 code bytes (read
+//     from LDS one stage ahead) and exactly one E8M0 scale byte per stage (one decode-table
+//     lookup for 32 weights). The scales are loaded to registers, 16 bytes a row (four
+//     super-stages) at a time. The weights are decoded in registers into the MFMA B operand.
+//   * Activation rows in LDS are 128 bytes with their 16-byte units XOR-swizzled by
+//     (r1, r0 ^ r2, r0 ^ r3); weight rows hold their 2S units XOR-ed with a function of the
+//     row, so the per-lane operand reads (16 consecutive rows, one unit) cover all 64 banks.
+// The MFMA K index is mapped so that lane half h of kq-step q holds K 32 S h + 32 s + 8 q +
+// (the pair-split order of 0..7) of super-stage stage s: the B lane's 32 weights are one
+// contiguous, single-scale block of its row, and the A operand reads unit 4 h + q of its row.
 // An expert's last tile is partial: the 32-row MFMA tiles past its rows are skipped
 // (wavefront-uniform branches); their activation loads fall out of range and return zeros.
 //
 // gate|up ("Round 7" brief, decision 4): a wavefront's two column tiles are the gate and up
 // rows of the same 32 channels, so bf16(silu(g) * u) is formed in registers; the workgroup
-// covers 128 channels. down ("Round 7" brief, decision 6; README "What had to be fixed"): the
+// covers 256 channels. down ("Round 7" brief, decision 6; README "What had to be fixed"): the
 // epilogue writes topk_w[p] * (I . Wd) in fp32.
 // Items (expert, 128-row block, weight-row block) are enumerated on the device from
 // expert_offsets; the persistent grid walks them so that the workgroups of one XCD take
@@ -38,14 +41,12 @@
 namespace moeq {
 
 constexpr int kPBM = 128, kPBK = 64;
-constexpr int kPThreads = 256;
+constexpr int kPThreads = 512;                    // 8 wavefronts
+constexpr int kPRowsW = 512;                      // weight rows of an item
 constexpr int kPATile = kPBM * kPBK * 2;          // one 128 x 64 bf16 activation tile: 16 KiB
+constexpr int kPABufs = 4;                        // activation tiles in LDS: DMA 3 stages ahead
+constexpr int kPWBytes = 64 * 1024;               // weight tiles in LDS (2 x 32 KiB or 4 x 16 KiB)
 constexpr uint32_t kPOutOfRange = 0x80000000u;
-// Weight loads use the default (cached) policy: a lane reads 32 of the 128 bytes of a cache
-// line per stage and the next three stages read the rest, and the items of the other row
-// tiles of the same expert read the same lines -- non-temporal loads made every stage fetch
-// its line from HBM again.
-constexpr int kPWeightPolicy = 0;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -117,31 +118,51 @@ __global__ void __launch_bounds__(256) pair_split_rows_kernel(const u32x4* __res
 #define MOEQ_WAIT_VMCNT(n) \
     __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
-// S: stages per weight super-stage. S = 4 when K % 128 == 0: a lane then reads the 64 code
-// bytes of its row for four stages at once (whole cache lines) and one aligned scale dword;
-// otherwise S = 1 (16 code bytes and the scale byte's dword per stage).
+// Workgroup barrier without a memory fence. __syncthreads() also makes the compiler wait for
+// every LDS-DMA load in flight, including the ones issued for stages ahead; the stage loop
+// instead waits for the one it needs with MOEQ_WAIT_VMCNT and relies on this barrier for the
+// rest: each wavefront consumes (waits for) every LDS read of a buffer before the barrier
+// after which that buffer is refilled. The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+#define MOEQ_STAGE_BARRIER()                 \
+    do {                                     \
+        asm volatile("" ::: "memory");       \
+        __builtin_amdgcn_s_barrier();        \
+        asm volatile("" ::: "memory");       \
+    } while (0)
+
+// S: stages per weight super-stage: 2 when K % 128 == 0 (a weight row's 64 code bytes of a
+// super-stage are one sector; its scale bytes are read 16 at a time, four super-stages), else
+// 1 (32 code bytes a row per stage, one scale byte per stage and lane).
 template <bool GATEUP, int S>
 __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
     prefill_kernel(const SkinnyArgs a) {
     constexpr int MT = 4, NT = 2;                 // 32 x 32 MFMA tiles per wavefront
+    constexpr int U = 2 * S;                      // 16-byte units of a weight row per super-stage
+    constexpr int WROW = 32 * S;                  // bytes of a weight row per super-stage
+    constexpr int NWB = 4 / S;                    // weight tiles in LDS
+    constexpr int WTILE = kPRowsW * WROW;         // bytes of one weight tile
+    static_assert(NWB * WTILE == kPWBytes, "weight tiles");
 
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int active[256];
     __shared__ int tpre[257];
     __shared__ int n_active_s;
     u32x4* tab = reinterpret_cast<u32x4*>(smem);
-    uint8_t* atile = smem + (size_t)a.tables.n * 256 * 16;       // [2][128 x 128 B]
+    uint8_t* atile = smem + (size_t)a.tables.n * 256 * 16;       // [kPABufs][128 x 128 B]
+    uint8_t* wtile = atile + kPABufs * kPATile;                   // [NWB][512 x WROW B]
     build_decode_tables(a.tables, tab);
     const int nact = p_active_tiles(a.offsets, a.E, active, tpre, &n_active_s);
 
     const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, cl = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int K = a.K, N = a.N;
-    const int cols = GATEUP ? 128 : 256;          // weight rows (gate|up: channels) per item
+    const int cols = GATEUP ? 256 : 512;          // output columns (gate|up: channels) per item
     const int ncb = (N + cols - 1) / cols;
     const long items = (long)__builtin_amdgcn_readfirstlane(tpre[nact]) * ncb;
     const int nstages = K / kPBK;
-    const int nsuper = (nstages + S - 1) / S;
+    const int nsuper = nstages / S;
+    const int ngroups = (nstages + 7) / 8;        // scale loads (S = 2): 8 stages each
     const uint32_t kb = (uint32_t)K / 2, ks = (uint32_t)K / 32;
     const uint32_t mcode = (uint32_t)N * kb, mscale = (uint32_t)N * ks;
     const __amdgpu_buffer_rsrc_t ract = p_rsrc(a.act, a.act_bytes);
@@ -153,13 +174,12 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
     const long slot = (G % 8 == 0) ? (long)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8
                                    : (long)blockIdx.x;
 
-    // MFMA A operand of kq-step q, row tile i: swz(32 i + cl, 4 h + q) = a_rd[q] + 4096 i (the
-    // swizzle depends on the row's low 4 bits only)
-    // ((4 h + q) ^ g = (4 h ^ g) ^ q for q < 4, so a_rd[q] = a_rd0 ^ 16 q)
+    // MFMA A operand of kq-step q, row tile i: swz(32 i + cl, 4 h + q) = a_rd0 ^ 16 q + 4096 i
+    // (the swizzle depends on the row's low 4 bits only; (4 h + q) ^ g = (4 h ^ g) ^ q)
     const int a_rd0 = swz(cl, 4 * h);
-    // Activation staging by LDS-DMA: load j (0..3) of wavefront w fills tile rows 32 w + 8 j ..
-    // + 7, lane L the 16 bytes at physical unit L % 8 of row 32 w + 8 j + L / 8, i.e. logical
-    // unit d_u[j % 2] (the row's low 4 bits are 8 (j % 2) + L / 8).
+    // Activation staging: load j (0, 1) of wavefront w fills tile rows 16 w + 8 j .. + 7, lane
+    // L the 16 bytes at physical unit L % 8 of row 16 w + 8 j + L / 8, i.e. logical unit
+    // d_u[j] (the row's low 4 bits are 8 j + L / 8).
     const int d_row = lane >> 3;
     int d_u[2];
 #pragma unroll
@@ -168,6 +188,24 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
         const int g = ((r >> 1) & 1) | (((r ^ (r >> 2)) & 1) << 1) | (((r ^ (r >> 3)) & 1) << 2);
         d_u[p] = (lane & 7) ^ g;
     }
+    // Weight tile rows: 0 .. 255 gate, 256 .. 511 up (same channels), or 512 down rows. Unit
+    // k of row R sits at position k ^ wsw(R), wsw(R) = (R / (16 / U)) % U: the 16 lanes of an
+    // operand read (rows R0 .. R0 + 15, one unit k) then hit 16 distinct bank groups.
+    auto wsw = [](int R) { return (R / (16 / U)) % U; };
+    // weight staging: load i (0 .. 2S - 1) of wavefront w fills rows 64 w + (64 / U) i + L / U,
+    // lane L position L % U
+    const int wd_t = lane % U;
+    // the tile rows of this lane's two column tiles, and the LDS offsets of its unit for
+    // stage s of a super-stage (unit S h + s)
+    uint32_t wr_off[NT][2];                       // [NT][S]
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int R = GATEUP ? j * 256 + 32 * wave + cl : 64 * wave + 32 * j + cl;
+#pragma unroll
+        for (int sp = 0; sp < S; ++sp)
+            wr_off[j][sp] = (uint32_t)(R * WROW + 16 * ((S * h + sp) ^ wsw(R)));
+    }
+    const uint32_t hsh = 16u * (uint32_t)h;       // S = 2: bit offset of the lane's scale bytes
 
     for (long item = slot; item < items; item += G) {
         const int tile = (int)(item / ncb), cb = (int)(item % ncb);
@@ -186,16 +224,14 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
         const bool badtab = tsel >= a.tables.n;
         const u32x4* mytab = tab + (badtab ? 0 : tsel) * 256;
 
-        // Stage st of super-stage m (st = S m + s, ms stages in m): unit u of an LDS row holds
-        // K = 64 S m + (u / 4) 32 ms + 32 s + 8 (u % 4) .. + 7, so that the lane half h of the
-        // B operand covers a contiguous 32 ms-wide K range of its weight row per super-stage.
-        // Row byte offset of a DMA lane: rb + 64 ms (u / 4) + 128 S m + 64 s.
+        // Stage st = S m + s: unit u of an activation row holds K = 64 S m + (u / 4) 32 S +
+        // 32 s + 8 (u % 4) .. + 7, i.e. row byte offset rb + 64 S (u / 4) + 128 S m + 64 s.
         // (rb is 16-byte aligned; its bit 0 carries u / 4, the K half of the lane's unit)
-        uint32_t rb[4];
+        uint32_t rb[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int rr = wave * 32 + j * 8 + d_row;
-            const int u = d_u[j & 1];
+        for (int j = 0; j < 2; ++j) {
+            const int rr = wave * 16 + j * 8 + d_row;
+            const int u = d_u[j];
             rb[j] = kPOutOfRange;
             if (rr < rows) {
                 const uint32_t src = GATEUP ? (uint32_t)(a.sorted_pair[r0 + rr] / a.k)
@@ -204,61 +240,66 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
             }
             rb[j] |= (uint32_t)(u >> 2);
         }
-        // the weight rows of this lane: column tile j of the wavefront
-        // (gate|up: both tiles use the same rows of the two matrices; down: the second tile
-        // starts 32 rows further)
-        __amdgpu_buffer_rsrc_t rc[NT], rs[NT];
-        const int wrow0 = GATEUP ? cb * 128 + wave * 32 + cl : cb * 256 + wave * 64 + cl;
-        const uint32_t cw0 = (uint32_t)wrow0 * kb, sw0 = (uint32_t)wrow0 * ks;
-        uint32_t cw[NT], sw[NT];
+        // weight staging sources (the wavefront's 64 tile rows are of one matrix)
+        const uint8_t* wmat = (GATEUP && wave >= 4) ? a.codes1 : a.codes0;
+        const __amdgpu_buffer_rsrc_t rcw = p_rsrc(wmat + (size_t)e * mcode, mcode);
+        uint32_t wdoff[4];          // [2 S] (a fixed size: hipcc's host pass drops the stubs of
+                                    // this kernel when a lambda captures a template-sized array)
+#pragma unroll
+        for (int i = 0; i < 2 * S; ++i) {
+            const int R = 64 * wave + (64 / U) * i + lane / U;
+            const int grow = GATEUP ? cb * 256 + (R & 255) : cb * 512 + R;
+            wdoff[i] = grow < N ? (uint32_t)grow * kb + 16u * (uint32_t)(wd_t ^ wsw(R))
+                                : kPOutOfRange;
+        }
+        // scale rows of the lane's column tiles
+        __amdgpu_buffer_rsrc_t rs[NT];
+        uint32_t sw[NT];
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            const int jr = GATEUP ? 0 : 32 * j;
-            const uint8_t* cm = (GATEUP && j == 1) ? a.codes1 : a.codes0;
             const uint8_t* sm = (GATEUP && j == 1) ? a.scales1 : a.scales0;
-            rc[j] = p_rsrc(cm + (size_t)e * mcode, mcode);
             rs[j] = p_rsrc(sm + (size_t)e * mscale, mscale);
-            cw[j] = wrow0 + jr < N ? cw0 + (uint32_t)jr * kb : kPOutOfRange;
-            sw[j] = wrow0 + jr < N ? sw0 + (uint32_t)jr * ks : kPOutOfRange;
+            const int srow = GATEUP ? cb * 256 + 32 * wave + cl : cb * 512 + 64 * wave + 32 * j + cl;
+            sw[j] = srow < N ? (uint32_t)srow * ks : kPOutOfRange;
         }
 
-        // Weights: chunk c (16 code bytes per column tile) of super-stage m is used at stage
-        // S m + c. For S = 4 the chunk registers are shared by consecutive super-stages: chunks
-        // 0, 1 of super-stage m + 1 (with its scale dwords, which alternate between two sets)
-        // are loaded at stage S m + 2, after chunks 0, 1 of m were used; chunks 2, 3 of
-        // m + 1 at its own stage 0. A row's 128-byte line is thus read in two bursts.
-        // (S = 1: two chunk slots alternate, slot = stage parity)
-        u32x4 wc[NT][S == 1 ? 2 : S];
-        uint32_t wsc[2][NT], wsh[2];
-        // Loads past the end re-read the last super-stage (cache hits, never used), so the
-        // stage loop has no branches around loads and the memory-counter waits stay exact.
-        auto wload = [&](int m, int c0, int nc, bool scales, int set) {
-            const int mc = min(m, nsuper - 1);
-            const uint32_t ms = (uint32_t)min(S, nstages - S * mc);
-            const uint32_t coff = 32u * S * (uint32_t)mc + 16u * ms * (uint32_t)h;
-            const uint32_t soff = 2u * S * (uint32_t)mc + ms * (uint32_t)h;
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-#pragma unroll
-                for (int c = c0; c < c0 + nc; ++c)       // S = 1: chunk 0 into slot c0
-                    wc[j][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                        rc[j], cw[j] + coff + 16u * (S == 1 ? 0 : c), 0, kPWeightPolicy));
-                if (scales)
-                    wsc[set][j] = __builtin_amdgcn_raw_buffer_load_b32(
-                        rs[j], (sw[j] + soff) & ~3u, 0, kPWeightPolicy);
-            }
-            if (scales) wsh[set] = ((sw[0] + soff) & 3u) * 8u;
-        };
-        auto dma = [&](int st) {
+        // ---- staging (steps past the end re-load the last stage: no branches around loads,
+        // so the memory-counter waits below stay exact) ----
+        auto dma_a = [&](int st, int pos) {          // activations of stage st -> tile pos % 4
             const int sc = min(st, nstages - 1);
             const int m = sc / S, sp = sc % S;
-            const uint32_t ms = (uint32_t)min(S, nstages - S * m);
             const uint32_t koff = 128u * S * (uint32_t)m + 64u * (uint32_t)sp;
-            uint8_t* dst = atile + (st & 1) * kPATile + wave * 4096;
+            uint8_t* dst = atile + (pos % kPABufs) * kPATile + wave * 2048;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    ract, dst + j * 1024, 16, (rb[j] & ~1u) + (rb[j] & 1u) * 64u * ms + koff, 0, 0, 0);
+                    ract, dst + j * 1024, 16, (rb[j] & ~1u) + (rb[j] & 1u) * 64u * S + koff, 0, 0, 0);
+        };
+        auto dma_w = [&](int msup, int mpos) {       // weights of super-stage msup -> tile mpos
+            const int mc = min(msup, nsuper - 1);
+            uint8_t* dst = wtile + (mpos % NWB) * WTILE + wave * 64 * WROW;
+#pragma unroll
+            for (int i = 0; i < 2 * S; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rcw, dst + i * 1024, 16,
+                                                         wdoff[i] + (uint32_t)WROW * mc, 0, 0, 0);
+        };
+        // scales: S = 2, 16 bytes a row (stages 8 g .. 8 g + 7; byte 4 (p / 2) + 2 h + p % 2 for
+        // stage 8 g + p); S = 1, one byte per stage in a ring of four
+        u32x4 wsc[NT], wscn[NT];
+        uint32_t wsb[NT][4];
+        auto sload2 = [&](int g, u32x4* dst) {
+            const int gc = min(g, ngroups - 1);
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                dst[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rs[j], sw[j] + 16u * (uint32_t)gc, 0, 0));
+        };
+        auto sload1 = [&](int st, int pos) {
+            const int sc = min(st, nstages - 1);
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                wsb[j][pos % 4] = __builtin_amdgcn_raw_buffer_load_b8(
+                    rs[j], sw[j] + 2u * (uint32_t)sc + (uint32_t)h, 0, 0);
         };
 
         f32x16 acc[MT][NT];
@@ -269,79 +310,124 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-        // FULL: all four 32-row MFMA tiles hold rows (no branches inside the stage)
-        // sp: sub-stage within the super-stage (scale byte), slot: chunk registers
-        auto compute = [&](auto full, int st, int set, int slot, int sp) {
-            constexpr bool FULL = decltype(full)::value;
-            const uint8_t* at = atile + (st & 1) * kPATile;
-            u32x4 t[NT];
+        // Operands in flight: the A fragments of the next kq-step (each 32-row fragment is
+        // re-read as soon as its MFMAs are issued), the decoded weights of this kq-step and the
+        // next, the lane's 16 code bytes and decode-table entries of one stage. A stage at
+        // unrolled position pos (0 .. 7; 8 = the next group's first) uses activation tile
+        // pos % 4 and weight tile (pos / S) % NWB.
+        u32x4 av[MT], b[2][NT], tt[NT], wcur[NT];
+        auto read_a = [&](int pos, int q, int i) {
+            const uint8_t* at = atile + (pos % kPABufs) * kPATile;
+            av[i] = *reinterpret_cast<const u32x4*>(at + (a_rd0 ^ (16 * q)) + i * 32 * 128);
+        };
+        auto read_w = [&](int pos) {
+            const uint8_t* wt = wtile + ((pos / S) % NWB) * WTILE;
 #pragma unroll
             for (int j = 0; j < NT; ++j)
-                t[j] = mytab[__builtin_amdgcn_ubfe(wsc[set][j], wsh[set] + 8u * sp, 8)];
-            // software pipeline over the four kq-steps: the A fragments and decoded weights of
-            // step q + 1 are produced while the MFMAs of step q run
-            u32x4 av[2][MT], b[2][NT];
-            auto read_a = [&](int q, u32x4* dst) {
+                wcur[j] = *reinterpret_cast<const u32x4*>(wt + wr_off[j][pos % S]);
+        };
+        auto tables_of = [&](int pos) {
 #pragma unroll
-                for (int i = 0; i < MT; ++i)
-                    if (FULL || i < mt_act)
-                        dst[i] = *reinterpret_cast<const u32x4*>(at + (a_rd0 ^ (16 * q)) + i * 32 * 128);
-            };
-            read_a(0, av[0]);
-#pragma unroll
-            for (int j = 0; j < NT; ++j) b[0][j] = decode8(wc[j][slot][0], t[j]);
+            for (int j = 0; j < NT; ++j) {
+                uint32_t sbyte;
+                if constexpr (S == 2) {
+                    const u32x4 src = pos >= 8 ? wscn[j] : wsc[j];
+                    const int p = pos % 8;
+                    sbyte = __builtin_amdgcn_ubfe(src[p / 2], hsh + 8u * (uint32_t)(p & 1), 8);
+                } else {
+                    sbyte = wsb[j][pos % 4];
+                }
+                tt[j] = mytab[sbyte];
+            }
+        };
+        // FULL: all four 32-row MFMA tiles hold rows (no branches inside the stage). Stage st
+        // (position pos) starts with its kq-step 0 operands in av, b[0]; in kq-step 2 it reads
+        // the code bytes and table entries of stage st + 1 (made visible by the barrier that
+        // closed stage st - 1) and in kq-step 3 its A fragments and first decoded weights, so
+        // the next stage starts with MFMAs at once.
+        auto compute = [&](auto full, int pos) {
+            constexpr bool FULL = decltype(full)::value;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int cur = q & 1, nxt = cur ^ 1;
-                if (q < 3) read_a(q + 1, av[nxt]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (q < 3) {
 #pragma unroll
-                    for (int j = 0; j < NT; ++j) b[nxt][j] = decode8(wc[j][slot][q + 1], t[j]);
-                }
-#pragma unroll
-                for (int i = 0; i < MT; ++i)
+                for (int i = 0; i < MT; ++i) {
                     if (FULL || i < mt_act)
 #pragma unroll
                         for (int j = 0; j < NT; ++j)
-                            acc[i][j] = mfma32x32x16(av[cur][i], b[cur][j], acc[i][j]);
-                __builtin_amdgcn_sched_barrier(0);
+                            acc[i][j] = mfma32x32x16(av[i], b[cur][j], acc[i][j]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (FULL || i < mt_act) {
+                        if (q < 3) read_a(pos, q + 1, i);
+                        else read_a(pos + 1, 0, i);
+                    }
+                    if (q < 3 && i < NT) b[nxt][i] = decode8(wcur[i][q + 1], tt[i]);
+                    if (q == 2 && i == 2) {
+                        tables_of(pos + 1);
+                        read_w(pos + 1);
+                    }
+                    if (q == 3 && i >= 2) b[nxt][i - 2] = decode8(wcur[i - 2][0], tt[i - 2]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         };
-        // Stage st: the activations of stage st + 1 go out by DMA into the other LDS buffer,
-        // then the weight loads of this stage (if any); stage st computes; the activations of
-        // stage st + 1 are waited for (loads return in order, so the weights issued after them
-        // stay in flight) and one barrier closes the stage. The scale sets alternate by
-        // unrolling two super-stages; the steps past the last stage only load.
+        // Stage st (position r of a group of 8): the activations of stage st + 3 go out by DMA
+        // into the tile stage st - 1 used; S = 2, odd r: the weights of super-stage
+        // (st + 3) / 2 into the tile super-stage (st - 1) / 2 used; r = 1: the next group's
+        // scales (S = 1: weights of stage st + 3 and scales of stage st + 2). Then stage st
+        // computes; what stage st + 1 reads in its last kq-steps (the activations of st + 2
+        // and the weights of its super-stage) is waited for -- loads return in order, so the
+        // ones issued after them stay in flight -- and one barrier closes the stage.
         auto run = [&](auto full) {
-            wload(0, 0, S == 4 ? 2 : 1, true, 0);
-            dma(0);
+#pragma unroll
+            for (int st = 0; st < 3; ++st) dma_a(st, st);
+            if constexpr (S == 2) {
+                dma_w(0, 0);
+                dma_w(1, 1);
+                sload2(0, wsc);
+            } else {
+#pragma unroll
+                for (int st = 0; st < 3; ++st) dma_w(st, st);
+                sload1(0, 0);
+                sload1(1, 1);
+            }
             MOEQ_WAIT_VMCNT(0);
             __syncthreads();
-            for (int st0 = 0; st0 < nstages; st0 += 2 * S) {
+            tables_of(0);
+            read_w(0);
 #pragma unroll
-                for (int r = 0; r < 2 * S; ++r) {
+            for (int i = 0; i < MT; ++i) read_a(0, 0, i);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) b[0][j] = decode8(wcur[j][0], tt[j]);
+            for (int st0 = 0; st0 < nstages; st0 += 8) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
                     const int st = st0 + r;
-                    const int m = st0 / S + r / S, sp = r % S, set = (r / S) & 1;
-                    dma(st + 1);
-                    int nw = 0;
-                    if (S == 1) {
-                        wload(m + 1, set ^ 1, 1, true, set ^ 1);
-                        nw = 2 * NT;
-                    } else if (sp == 0) {
-                        wload(m, 2, 2, false, set);
-                        nw = 2 * NT;
-                    } else if (sp == 2) {
-                        wload(m + 1, 0, 2, true, set ^ 1);
-                        nw = 3 * NT;
+                    dma_a(st + 3, r + 3);
+                    if constexpr (S == 2) {
+                        if (r & 1) dma_w((st + 3) / 2, (r + 3) / 2);
+                        if (r == 1) sload2(st0 / 8 + 1, wscn);
+                    } else {
+                        dma_w(st + 3, r + 3);
+                        sload1(st + 2, r + 2);
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    if (st < nstages) compute(full, st, set, S == 1 ? set : sp, sp);
+                    if (st < nstages) compute(full, r);
                     __builtin_amdgcn_sched_barrier(0);
-                    if (nw == 3 * NT) MOEQ_WAIT_VMCNT(3 * NT);
-                    else if (nw == 2 * NT) MOEQ_WAIT_VMCNT(2 * NT);
-                    else MOEQ_WAIT_VMCNT(0);
-                    __syncthreads();
+                    if constexpr (S == 2) {
+                        if (r == 7) {
+#pragma unroll
+                            for (int j = 0; j < NT; ++j) wsc[j] = wscn[j];
+                        }
+                    }
+                    // loads issued after the last one waited for
+                    constexpr int kLater[2][8] = {{8, 8, 8, 8, 8, 8, 8, 8}, {2, 8, 4, 6, 2, 6, 2, 6}};
+                    const int nlater = kLater[S - 1][r];
+                    if (nlater == 8) MOEQ_WAIT_VMCNT(8);
+                    else if (nlater == 6) MOEQ_WAIT_VMCNT(6);
+                    else if (nlater == 4) MOEQ_WAIT_VMCNT(4);
+                    else MOEQ_WAIT_VMCNT(2);
+                    MOEQ_STAGE_BARRIER();
                 }
             }
         };
@@ -354,7 +440,7 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
         asm volatile("" : "+v"(el));              // computed here, not kept live across the loop
         const int hr = 4 * (el >> 5), ecl = el & 31;
         if (GATEUP) {
-            const int ch = cb * 128 + wave * 32 + ecl;
+            const int ch = cb * 256 + wave * 32 + ecl;
             const int slotc = (ch & ~7) | (((ch & 1) << 2) | ((ch & 7) >> 1));
             uint16_t* ob = reinterpret_cast<uint16_t*>(a.out) + (size_t)(r0 + hr) * a.out_ld + slotc;
 #pragma unroll
@@ -370,7 +456,7 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
                 }
             }
         } else {
-            const int col = cb * 256 + wave * 64 + ecl;
+            const int col = cb * 512 + wave * 64 + ecl;
             float* ob = reinterpret_cast<float*>(a.out) + (size_t)(r0 + hr) * a.out_ld + col;
             const int32_t* sp = a.sorted_pair + r0 + hr;
 #pragma unroll
@@ -404,9 +490,9 @@ void launch_pair_split_rows(const uint16_t* x, int T, int H, uint16_t* xs, int c
 
 // tiles: host upper bound of the 128-row tiles the device will find
 void launch_prefill(const SkinnyArgs& a, bool gateup, long tiles, int cus, hipStream_t stream) {
-    const size_t lds = (size_t)a.tables.n * 256 * 16 + 2 * kPATile;
-    const long ncb = gateup ? (a.N + 127) / 128 : (a.N + 255) / 256;
-    long blocks = std::min(tiles * ncb, (long)cus * 2);
+    const size_t lds = (size_t)a.tables.n * 256 * 16 + kPABufs * kPATile + kPWBytes;
+    const long ncb = gateup ? (a.N + 255) / 256 : (a.N + 511) / 512;
+    long blocks = std::min(tiles * ncb, (long)cus);
     if (blocks >= 8) blocks -= blocks % 8;                       // whole rounds over the XCDs
     blocks = std::max(1L, blocks);
     const bool wide = a.K % 128 == 0;
@@ -414,9 +500,9 @@ void launch_prefill(const SkinnyArgs& a, bool gateup, long tiles, int cus, hipSt
         hipLaunchKernelGGL(kern, dim3(blocks), dim3(kPThreads), lds, stream, a);
     };
     if (gateup) {
-        if (wide) go(prefill_kernel<true, 4>); else go(prefill_kernel<true, 1>);
+        if (wide) go(prefill_kernel<true, 2>); else go(prefill_kernel<true, 1>);
     } else {
-        if (wide) go(prefill_kernel<false, 4>); else go(prefill_kernel<false, 1>);
+        if (wide) go(prefill_kernel<false, 2>); else go(prefill_kernel<false, 1>);
     }
 }
 
