@@ -131,6 +131,15 @@ __global__ void __launch_bounds__(256) pair_split_rows_kernel(const u32x4* __res
         asm volatile("" ::: "memory");       \
     } while (0)
 
+// Stage-loop waits, by S and stage position r in a group of 8: the number of vector-memory
+// loads issued after the one waited for (loads return in order; the issue schedule is the
+// one of prefill_kernel's issue()). kPWaitA: before the barrier of stage st, for the
+// activations of stage st + 1 (issued in stage st - 3); kPWaitW: before the code bytes of
+// stage st + 1 are read, for their weights (issued in stage st - 3; S = 2: odd r only, when
+// stage st + 1 starts a super-stage; 0 = no wait).
+constexpr int kPWaitA[2][8] = {{16, 16, 16, 16, 16, 16, 16, 16}, {8, 12, 10, 14, 10, 12, 8, 12}};
+constexpr int kPWaitW[2][8] = {{14, 14, 14, 14, 14, 14, 14, 14}, {0, 8, 0, 10, 0, 8, 0, 8}};
+
 // S: stages per weight super-stage: 2 when K % 128 == 0 (a weight row's 64 code bytes of a
 // super-stage are one sector; its scale bytes are read 16 at a time, four super-stages), else
 // 1 (32 code bytes a row per stage, one scale byte per stage and lane).
@@ -192,8 +201,15 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
     // k of row R sits at position k ^ wsw(R), wsw(R) = (R / (16 / U)) % U: the 16 lanes of an
     // operand read (rows R0 .. R0 + 15, one unit k) then hit 16 distinct bank groups.
     auto wsw = [](int R) { return (R / (16 / U)) % U; };
-    // weight staging: load i (0 .. 2S - 1) of wavefront w fills rows 64 w + (64 / U) i + L / U,
-    // lane L position L % U
+    // weight staging: load i (0 .. 2S - 1) of a wavefront fills the 32 / S tile rows from
+    // wd_row0[i], lane L row wd_row0[i] + L / U, position L % U (fixed-size arrays throughout:
+    // hipcc's host pass drops this kernel's stubs when its lambdas capture template-sized
+    // arrays or call one another)
+    int wd_row0[4];
+#pragma unroll
+    for (int i = 0; i < 2 * S; ++i)
+        wd_row0[i] = GATEUP ? (i < S ? 32 * wave + (32 / S) * i : 256 + 32 * wave + (32 / S) * (i - S))
+                            : 64 * wave + (32 / S) * i;
     const int wd_t = lane % U;
     // the tile rows of this lane's two column tiles, and the LDS offsets of its unit for
     // stage s of a super-stage (unit S h + s)
@@ -240,14 +256,16 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
             }
             rb[j] |= (uint32_t)(u >> 2);
         }
-        // weight staging sources (the wavefront's 64 tile rows are of one matrix)
-        const uint8_t* wmat = (GATEUP && wave >= 4) ? a.codes1 : a.codes0;
-        const __amdgpu_buffer_rsrc_t rcw = p_rsrc(wmat + (size_t)e * mcode, mcode);
-        uint32_t wdoff[4];          // [2 S] (a fixed size: hipcc's host pass drops the stubs of
-                                    // this kernel when a lambda captures a template-sized array)
+        // weight staging sources: a wavefront stages exactly the 64 tile rows it reads (gate|up:
+        // loads 0 .. S - 1 its gate rows, S .. 2S - 1 its up rows), so the weights need no
+        // barrier, only the wavefront's own memory-counter waits
+        const __amdgpu_buffer_rsrc_t rcw0 = p_rsrc(a.codes0 + (size_t)e * mcode, mcode);
+        const __amdgpu_buffer_rsrc_t rcw1 =
+            GATEUP ? p_rsrc(a.codes1 + (size_t)e * mcode, mcode) : rcw0;
+        uint32_t wdoff[4];                        // [2 S]
 #pragma unroll
         for (int i = 0; i < 2 * S; ++i) {
-            const int R = 64 * wave + (64 / U) * i + lane / U;
+            const int R = wd_row0[i] + lane / U;
             const int grow = GATEUP ? cb * 256 + (R & 255) : cb * 512 + R;
             wdoff[i] = grow < N ? (uint32_t)grow * kb + 16u * (uint32_t)(wd_t ^ wsw(R))
                                 : kPOutOfRange;
@@ -277,10 +295,11 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
         };
         auto dma_w = [&](int msup, int mpos) {       // weights of super-stage msup -> tile mpos
             const int mc = min(msup, nsuper - 1);
-            uint8_t* dst = wtile + (mpos % NWB) * WTILE + wave * 64 * WROW;
+            uint8_t* dst = wtile + (mpos % NWB) * WTILE;
 #pragma unroll
             for (int i = 0; i < 2 * S; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rcw, dst + i * 1024, 16,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(i < S ? rcw0 : rcw1,
+                                                         dst + wd_row0[i] * WROW, 16,
                                                          wdoff[i] + (uint32_t)WROW * mc, 0, 0, 0);
         };
         // scales: S = 2, 16 bytes a row (stages 8 g .. 8 g + 7; byte 4 (p / 2) + 2 h + p % 2 for
@@ -340,12 +359,39 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
                 tt[j] = mytab[sbyte];
             }
         };
+        // Loads issued in stage st (position r of a group of 8 stages), after its barrier: the
+        // activations of stage st + 4 (into the tile of stage st); S = 2: for even r the weights
+        // of super-stage st / 2 + 2 (into the tile of super-stage st / 2), for r = 1 the next
+        // group's scales; S = 1: the weights of stage st + 4 and the scale bytes of stage st + 3.
+        auto issue = [&](int st, int r) {
+            dma_a(st + 4, r + 4);
+            if (S == 2) {
+                if ((r & 1) == 0) dma_w(st / 2 + 2, r / 2 + 2);
+                if (r == 1) sload2(st / 8 + 1, wscn);
+            } else {
+                dma_w(st + 4, r + 4);
+                sload1(st + 3, r + 3);
+            }
+        };
+        // waits: kPWaitA / kPWaitW (namespace scope)
+        auto wait_n = [](int n) {
+            switch (n) {
+                case 16: MOEQ_WAIT_VMCNT(16); break;
+                case 14: MOEQ_WAIT_VMCNT(14); break;
+                case 12: MOEQ_WAIT_VMCNT(12); break;
+                case 10: MOEQ_WAIT_VMCNT(10); break;
+                case 8: MOEQ_WAIT_VMCNT(8); break;
+                default: MOEQ_WAIT_VMCNT(0); break;
+            }
+        };
         // FULL: all four 32-row MFMA tiles hold rows (no branches inside the stage). Stage st
-        // (position pos) starts with its kq-step 0 operands in av, b[0]; in kq-step 2 it reads
-        // the code bytes and table entries of stage st + 1 (made visible by the barrier that
-        // closed stage st - 1) and in kq-step 3 its A fragments and first decoded weights, so
-        // the next stage starts with MFMAs at once.
-        auto compute = [&](auto full, int pos) {
+        // (position r) starts with its kq-step 0 operands in av, b[0]. In kq-step 2 it reads the
+        // code bytes and table entries of stage st + 1 (its own staged weights); after kq-step 2
+        // (the last reads of its activation tile) the workgroup barrier makes the activations
+        // of stage st + 1 visible and frees the tile of stage st, which the loads of the stage
+        // then refill; kq-step 3 fetches the A fragments and first decoded weights of stage
+        // st + 1, so the next stage starts with MFMAs at once.
+        auto compute = [&](auto full, int st, int r) {
             constexpr bool FULL = decltype(full)::value;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -356,40 +402,41 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
                         for (int j = 0; j < NT; ++j)
                             acc[i][j] = mfma32x32x16(av[i], b[cur][j], acc[i][j]);
-                    __builtin_amdgcn_sched_barrier(0);
                     if (FULL || i < mt_act) {
-                        if (q < 3) read_a(pos, q + 1, i);
-                        else read_a(pos + 1, 0, i);
+                        if (q < 3) read_a(r, q + 1, i);
+                        else read_a(r + 1, 0, i);
                     }
                     if (q < 3 && i < NT) b[nxt][i] = decode8(wcur[i][q + 1], tt[i]);
                     if (q == 2 && i == 2) {
-                        tables_of(pos + 1);
-                        read_w(pos + 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (kPWaitW[S - 1][r]) wait_n(kPWaitW[S - 1][r]);
+                        asm volatile("" ::: "memory");
+                        tables_of(r + 1);
+                        read_w(r + 1);
                     }
                     if (q == 3 && i >= 2) b[nxt][i - 2] = decode8(wcur[i - 2][0], tt[i - 2]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (q == 2) {
+                    wait_n(kPWaitA[S - 1][r]);
+                    MOEQ_STAGE_BARRIER();
+                    issue(st, r);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
-        // Stage st (position r of a group of 8): the activations of stage st + 3 go out by DMA
-        // into the tile stage st - 1 used; S = 2, odd r: the weights of super-stage
-        // (st + 3) / 2 into the tile super-stage (st - 1) / 2 used; r = 1: the next group's
-        // scales (S = 1: weights of stage st + 3 and scales of stage st + 2). Then stage st
-        // computes; what stage st + 1 reads in its last kq-steps (the activations of st + 2
-        // and the weights of its super-stage) is waited for -- loads return in order, so the
-        // ones issued after them stay in flight -- and one barrier closes the stage.
         auto run = [&](auto full) {
 #pragma unroll
-            for (int st = 0; st < 3; ++st) dma_a(st, st);
-            if constexpr (S == 2) {
+            for (int st = 0; st < 4; ++st) dma_a(st, st);
+            if (S == 2) {
                 dma_w(0, 0);
                 dma_w(1, 1);
                 sload2(0, wsc);
             } else {
 #pragma unroll
-                for (int st = 0; st < 3; ++st) dma_w(st, st);
-                sload1(0, 0);
-                sload1(1, 1);
+                for (int st = 0; st < 4; ++st) dma_w(st, st);
+#pragma unroll
+                for (int st = 0; st < 3; ++st) sload1(st, st);
             }
             MOEQ_WAIT_VMCNT(0);
             __syncthreads();
@@ -399,37 +446,27 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
             for (int i = 0; i < MT; ++i) read_a(0, 0, i);
 #pragma unroll
             for (int j = 0; j < NT; ++j) b[0][j] = decode8(wcur[j][0], tt[j]);
-            for (int st0 = 0; st0 < nstages; st0 += 8) {
+            // whole groups of 8 stages as straight-line code (branches between the loads would
+            // make the compiler's own waits for the scale registers drain every load in flight),
+            // then the last group's stages one by one
+            int st0 = 0;
+            for (; st0 + 8 <= nstages; st0 += 8) {
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int st = st0 + r;
-                    dma_a(st + 3, r + 3);
-                    if constexpr (S == 2) {
-                        if (r & 1) dma_w((st + 3) / 2, (r + 3) / 2);
-                        if (r == 1) sload2(st0 / 8 + 1, wscn);
-                    } else {
-                        dma_w(st + 3, r + 3);
-                        sload1(st + 2, r + 2);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (st < nstages) compute(full, r);
-                    __builtin_amdgcn_sched_barrier(0);
-                    if constexpr (S == 2) {
-                        if (r == 7) {
+                for (int r = 0; r < 8; ++r) compute(full, st0 + r, r);
+                if (S == 2) {
 #pragma unroll
-                            for (int j = 0; j < NT; ++j) wsc[j] = wscn[j];
-                        }
-                    }
-                    // loads issued after the last one waited for
-                    constexpr int kLater[2][8] = {{8, 8, 8, 8, 8, 8, 8, 8}, {2, 8, 4, 6, 2, 6, 2, 6}};
-                    const int nlater = kLater[S - 1][r];
-                    if (nlater == 8) MOEQ_WAIT_VMCNT(8);
-                    else if (nlater == 6) MOEQ_WAIT_VMCNT(6);
-                    else if (nlater == 4) MOEQ_WAIT_VMCNT(4);
-                    else MOEQ_WAIT_VMCNT(2);
-                    MOEQ_STAGE_BARRIER();
+                    for (int j = 0; j < NT; ++j) wsc[j] = wscn[j];
                 }
             }
+            if (st0 < nstages) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    if (st0 + r < nstages) compute(full, st0 + r, r);
+            }
+            // the last stage's kq-step 3 read the (unused) tile past the end: all wavefronts
+            // are done with LDS before the next item stages into it
+            MOEQ_WAIT_VMCNT(0);
+            __syncthreads();
         };
         if (mt_act == MT) run(std::true_type{});
         else run(std::false_type{});
