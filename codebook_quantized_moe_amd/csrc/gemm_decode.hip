@@ -349,13 +349,19 @@ decode_kernel(const SkinnyArgs a) {
             for (int j = 0; j < 4; ++j) A[j] = *reinterpret_cast<const u32x4*>(ap + 16 * j);
             const uint8_t* sp = sbuf + buf * kSBufBytes + (kk % kChunkK) / 32 + b;
             const bool kin = kk + 32 * b < K;
+            // the four scale bytes, then their four table entries: two LDS round trips per
+            // K-step instead of two per group
+            uint32_t sc[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) sc[g] = kin ? (uint32_t)sp[soff[g]] : 0u;
+            u32x4 t[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) t[g] = mytab[sc[g]];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const uint32_t sc = kin ? (uint32_t)sp[soff[g]] : 0u;
-                const u32x4 t = mytab[sc];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const u32x4 w = decode8(c[g][j], t);
+                    const u32x4 w = decode8(c[g][j], t[g]);
                     acc[g] = mfma4x4x4(A[j][0], A[j][1], w[0], w[1], acc[g]);
                     acc[g] = mfma4x4x4(A[j][2], A[j][3], w[2], w[3], acc[g]);
                 }
