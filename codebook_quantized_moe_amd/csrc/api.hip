@@ -114,12 +114,6 @@ bool use_prefill_path(int T, int k, int E) {
     return (long long)T * k >= 16LL * E;     // >= 16 rows per expert on average
 }
 
-int persistent_blocks(long wg_items) {
-    const long cap = (long)cu_count() * 2;
-    long b = wg_items;
-    if (b > cap) b = cap;
-    return (int)(b < 1 ? 1 : b);
-}
 
 
 }  // namespace
@@ -130,9 +124,9 @@ const char* moeq_last_error(void) { return g_err; }
 
 size_t moeq_workspace_bytes(int T, int k, int E, int H, int I) {
     (void)k; (void)E; (void)I;
-    // gate|up stages x in pair-split order
+    // the prefill kernels' work-queue counters, then x in pair-split order (gate|up)
     if (T <= 0 || H <= 0) return 0;
-    return prefill_split_bytes(T, H);
+    return prefill_queue_bytes() + prefill_split_bytes(T, H);
 }
 
 int moeq_route_topk(const float* logits, int T, int E, int k, int gating, int32_t* topk_ids,
@@ -203,18 +197,20 @@ static int projection(const char* w, bool gateup, const uint16_t* act, int T, in
     a.K = gateup ? H : I;
     a.out_ld = gateup ? I : H;
 
+    a.queue = static_cast<int32_t*>(ws);
     const long touched = (long)(E < T * k ? E : T * k);
     clear_hip_error();
     if (gateup) {
         // both projection families read x in the decoder's pair-split K order
-        uint16_t* xs = static_cast<uint16_t*>(ws);
+        uint16_t* xs = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + prefill_queue_bytes());
         launch_pair_split_rows(static_cast<const uint16_t*>(act), T, H, xs, cu_count(), stream);
         a.act = xs;
     }
     if (use_prefill_path(T, k, E)) {
         // upper bound of the 128-row tiles the device will find
         const long tiles = touched + (long)T * k / prefill_tile_rows();
-        launch_prefill(a, gateup, tiles, cu_count(), stream);
+        const char* groups_env = getenv("MOEQ_PREFILL_WORKGROUPS");   // testing only
+        launch_prefill(a, gateup, tiles, cu_count(), groups_env ? atoi(groups_env) : 0, stream);
     } else {
         // upper bound of the 4-row tiles the device will find
         const long tiles = touched + (long)T * k / decode_tile_rows();

@@ -47,6 +47,7 @@ constexpr int kPATile = kPBM * kPBK * 2;          // one 128 x 64 bf16 activatio
 constexpr int kPABufs = 4;                        // activation tiles in LDS: DMA 3 stages ahead
 constexpr int kPWBytes = 64 * 1024;               // weight tiles in LDS (2 x 32 KiB or 4 x 16 KiB)
 constexpr uint32_t kPOutOfRange = 0x80000000u;
+constexpr int kPQueues = 8;                       // work queues, one per XCD
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -176,12 +177,14 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
     const uint32_t mcode = (uint32_t)N * kb, mscale = (uint32_t)N * ks;
     const __amdgpu_buffer_rsrc_t ract = p_rsrc(a.act, a.act_bytes);
 
-    // XCD-contiguous walk: workgroup g runs on XCD g % 8; the workgroups of one XCD take a
-    // contiguous run of items each round
-    const long G = gridDim.x;
-    const long per_xcd = G / 8;
-    const long slot = (G % 8 == 0) ? (long)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8
-                                   : (long)blockIdx.x;
+    // Work queues: a.queue holds one counter per XCD (zero at launch; workgroup g runs on XCD
+    // g % 8). Queue x hands out, in order, the items of item groups x, x + 8, x + 16, ..., a
+    // group being the column blocks of 4 row tiles, which share activations and weights in the
+    // XCD's L2. A workgroup drains its own XCD's queue first, then the other queues, so the
+    // work balances across workgroups whatever the items cost.
+    const int myx = (int)(blockIdx.x % 8);
+    const long grp = 4L * ncb;
+    __shared__ int s_claim;
 
     // MFMA A operand of kq-step q, row tile i: swz(32 i + cl, 4 h + q) = a_rd0 ^ 16 q + 4096 i
     // (the swizzle depends on the row's low 4 bits only; (4 h + q) ^ g = (4 h ^ g) ^ q)
@@ -223,8 +226,26 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
     }
     const uint32_t hsh = 16u * (uint32_t)h;       // S = 2: bit offset of the lane's scale bytes
 
-    for (long item = slot; item < items; item += G) {
+    // s_claim is written by thread 0 only after a barrier that every wavefront reaches after
+    // reading its previous value: the staging barrier of an item, or the barrier below when a
+    // queue is drained (the previous item's epilogue ends without one).
+    int qx = 0;                                   // queues drained: myx .. myx + qx - 1
+    if (tid == 0) s_claim = atomicAdd(&a.queue[myx], 1);
+    __syncthreads();
+    int claim = __builtin_amdgcn_readfirstlane(s_claim);
+    for (;;) {
+        const int qcur = (myx + qx) & 7;
+        const long item = ((long)(claim / grp) * 8 + qcur) * grp + claim % grp;
+        if (item >= items) {                      // queue qcur is drained: take the next one
+            if (++qx == 8) break;
+            __syncthreads();                      // every wavefront has read the last claim
+            if (tid == 0) s_claim = atomicAdd(&a.queue[(myx + qx) & 7], 1);
+            __syncthreads();
+            claim = __builtin_amdgcn_readfirstlane(s_claim);
+            continue;
+        }
         const int tile = (int)(item / ncb), cb = (int)(item % ncb);
+        int nclaim = 0;                           // the next claim of queue qcur (thread 0)
         int lo = 0, hi = nact - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -440,6 +461,7 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
             }
             MOEQ_WAIT_VMCNT(0);
             __syncthreads();
+            if (tid == 0) s_claim = nclaim;           // read by all after the item's last barrier
             tables_of(0);
             read_w(0);
 #pragma unroll
@@ -468,6 +490,9 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
             MOEQ_WAIT_VMCNT(0);
             __syncthreads();
         };
+        // the next item of this queue is claimed now: the staging's wait covers the atomic,
+        // and its result is published after the staging's barrier
+        if (tid == 0) nclaim = atomicAdd(&a.queue[qcur], 1);
         if (mt_act == MT) run(std::true_type{});
         else run(std::false_type{});
 
@@ -510,12 +535,19 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
                 }
             }
         }
+        claim = __builtin_amdgcn_readfirstlane(s_claim);
     }
+}
+
+__global__ void __launch_bounds__(64) zero_queue_kernel(int32_t* q) {
+    if (threadIdx.x < kPQueues) q[threadIdx.x] = 0;
 }
 
 int prefill_tile_rows() { return kPBM; }
 
 size_t prefill_split_bytes(int T, int H) { return ((size_t)T * H * 2 + 255) & ~(size_t)255; }
+
+size_t prefill_queue_bytes() { return 256; }
 
 void launch_pair_split_rows(const uint16_t* x, int T, int H, uint16_t* xs, int cus,
                             hipStream_t stream) {
@@ -526,11 +558,14 @@ void launch_pair_split_rows(const uint16_t* x, int T, int H, uint16_t* xs, int c
 }
 
 // tiles: host upper bound of the 128-row tiles the device will find
-void launch_prefill(const SkinnyArgs& a, bool gateup, long tiles, int cus, hipStream_t stream) {
+void launch_prefill(const SkinnyArgs& a, bool gateup, long tiles, int cus, int max_groups,
+                    hipStream_t stream) {
+    hipLaunchKernelGGL(zero_queue_kernel, dim3(1), dim3(64), 0, stream, a.queue);
     const size_t lds = (size_t)a.tables.n * 256 * 16 + kPABufs * kPATile + kPWBytes;
     const long ncb = gateup ? (a.N + 255) / 256 : (a.N + 511) / 512;
     long blocks = std::min(tiles * ncb, (long)cus);
     if (blocks >= 8) blocks -= blocks % 8;                       // whole rounds over the XCDs
+    if (max_groups > 0) blocks = std::min(blocks, (long)max_groups);
     blocks = std::max(1L, blocks);
     const bool wide = a.K % 128 == 0;
     auto go = [&](auto kern) {

@@ -24,6 +24,7 @@ struct SkinnyArgs {
     int N;                        // weight rows per expert: I (gate|up) or H (down)
     int K;                        // contraction length: H (gate|up) or I (down)
     int out_ld;                   // row stride of out, in elements
+    int32_t* queue;               // prefill: 8 work-queue counters (device, zeroed per launch)
     TableArgs tables;
 };
 
@@ -34,9 +35,12 @@ void launch_permute(const int32_t* ids, int P, int E, int32_t* offsets, int32_t*
 void launch_decode(const SkinnyArgs& a, bool gateup, long tiles, int cus, int shape,
                    hipStream_t stream);
 int decode_tile_rows();
-void launch_prefill(const SkinnyArgs& a, bool gateup, long tiles, int cus, hipStream_t stream);
+// max_groups > 0 caps the workgroups (testing: many items per workgroup)
+void launch_prefill(const SkinnyArgs& a, bool gateup, long tiles, int cus, int max_groups,
+                    hipStream_t stream);
 int prefill_tile_rows();
 size_t prefill_split_bytes(int T, int H);
+size_t prefill_queue_bytes();
 void launch_pair_split_rows(const uint16_t* x, int T, int H, uint16_t* xs, int cus,
                             hipStream_t stream);
 void launch_combine(const float* yp, const int32_t* pair_pos, const int32_t* offsets, int T, int k,

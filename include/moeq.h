@@ -72,10 +72,12 @@ static inline int moeq_inter_slot(int c) {
 const char* moeq_last_error(void);
 
 /* Bytes of device workspace that moeq_gateup_swiglu and moeq_down need for these sizes
- * (0 means they accept ws = NULL). Currently T * H * 2 rounded up to 256: gate|up first
- * writes a copy of x with every 8-element group in the pair-split order of moeq_inter_slot
- * into it. The workspace must be 16-byte aligned; its contents are scratch
- * between calls (two calls that run at the same time need two workspaces). */
+ * (0 means they accept ws = NULL). Currently 256 + T * H * 2 rounded up to 256: the first
+ * 256 bytes hold the work-queue counters of the many-rows kernels (the call clears them on
+ * its stream before use), the rest a copy of x that gate|up writes with every 8-element
+ * group in the pair-split order of moeq_inter_slot. The workspace must be 16-byte aligned;
+ * its contents are scratch between calls (two calls that run at the same time need two
+ * workspaces). */
 size_t moeq_workspace_bytes(int T, int k, int E, int H, int I);
 
 /*

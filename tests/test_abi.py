@@ -123,9 +123,10 @@ def test_last_error_is_cleared_on_success():
 
 
 def test_workspace_contract():
-    # T * H bf16 values (the pair-split copy of x), rounded up to 256 bytes; 0 for T = 0
-    assert mq.moeq_workspace_bytes(8, 8, 256, 6144, 2048) == 8 * 6144 * 2
-    assert mq.moeq_workspace_bytes(3, 8, 256, 64, 64) == 512
+    # 256 bytes of work-queue counters + T * H bf16 values (the pair-split copy of x),
+    # rounded up to 256 bytes; 0 for T = 0
+    assert mq.moeq_workspace_bytes(8, 8, 256, 6144, 2048) == 256 + 8 * 6144 * 2
+    assert mq.moeq_workspace_bytes(3, 8, 256, 64, 64) == 256 + 512
     assert mq.moeq_workspace_bytes(0, 8, 256, 6144, 2048) == 0
     need = mq.moeq_workspace_bytes(8, 8, 256, 6144, 2048)
     assert _status(mq.moeq_gateup_swiglu, **_gateup()) == mq.MOEQ_EWORKSPACE

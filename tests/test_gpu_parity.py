@@ -220,6 +220,20 @@ def test_layer_ragged_shapes(T, E, H, I, k, path):
     check_layer(out, ref, k)
 
 
+@pytest.mark.parametrize("groups", [1, 3])
+@pytest.mark.parametrize("T,E,H,I,k", [(64, 4, 256, 192, 4), (1, 16, 256, 128, 16),
+                                       (37, 8, 576, 320, 4)])
+def test_layer_prefill_few_workgroups(T, E, H, I, k, groups, monkeypatch):
+    """The many-rows kernels with every item on one (or three) workgroups: consecutive items
+    and drained work queues on one workgroup (a claim race here once mixed up items)."""
+    monkeypatch.setenv("MOEQ_FORCE_PATH", "prefill")
+    monkeypatch.setenv("MOEQ_PREFILL_WORKGROUPS", str(groups))
+    lw, x, logits = _case(24, T, E, H, I, k, e2m1_experts=(1,), permute="random")
+    out = run_layer(lw, x, logits, k)
+    ref = oracle.layer_forward(x, logits, k, lw)
+    check_layer(out, ref, k)
+
+
 def test_layer_residual_in_place(path):
     mq = _mq()
     T, E, H, I, k = 16, 4, 256, 128, 2
