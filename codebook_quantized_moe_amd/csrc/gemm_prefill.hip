@@ -185,6 +185,7 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
     const int myx = (int)(blockIdx.x % 8);
     const long grp = 4L * ncb;
     __shared__ int s_claim;
+    __shared__ float s_roww[kPBM];                // down: topk_w of the item's rows
 
     // MFMA A operand of kq-step q, row tile i: swz(32 i + cl, 4 h + q) = a_rd0 ^ 16 q + 4096 i
     // (the swizzle depends on the row's low 4 bits only; (4 h + q) ^ g = (4 h ^ g) ^ q)
@@ -246,6 +247,8 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
         }
         const int tile = (int)(item / ncb), cb = (int)(item % ncb);
         int nclaim = 0;                           // the next claim of queue qcur (thread 0)
+        int row_pair = 0;                         // down, thread t < 128: pair of row t
+        float row_w = 0.f;                        // and its router weight
         int lo = 0, hi = nact - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -462,6 +465,7 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
             MOEQ_WAIT_VMCNT(0);
             __syncthreads();
             if (tid == 0) s_claim = nclaim;           // read by all after the item's last barrier
+            if (!GATEUP && tid < kPBM && tid < rows) row_w = a.topk_w[row_pair];
             tables_of(0);
             read_w(0);
 #pragma unroll
@@ -485,6 +489,7 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
                 for (int r = 0; r < 8; ++r)
                     if (st0 + r < nstages) compute(full, st0 + r, r);
             }
+            if (!GATEUP && tid < kPBM) s_roww[tid] = row_w;
             // the last stage's kq-step 3 read the (unused) tile past the end: all wavefronts
             // are done with LDS before the next item stages into it
             MOEQ_WAIT_VMCNT(0);
@@ -493,6 +498,11 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
         // the next item of this queue is claimed now: the staging's wait covers the atomic,
         // and its result is published after the staging's barrier
         if (tid == 0) nclaim = atomicAdd(&a.queue[qcur], 1);
+        // down: thread t < 128 fetches the router weight of row t (its pair index now, under
+        // the staging's wait; the weight after the staging barrier) and parks it in LDS at the
+        // end of the stage loop, where the load has long arrived: the epilogue then reads LDS
+        // instead of two dependent global loads per output row
+        if (!GATEUP && tid < kPBM && tid < rows) row_pair = a.sorted_pair[r0 + tid];
         if (mt_act == MT) run(std::true_type{});
         else run(std::false_type{});
 
@@ -520,7 +530,6 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
         } else {
             const int col = cb * 512 + wave * 64 + ecl;
             float* ob = reinterpret_cast<float*>(a.out) + (size_t)(r0 + hr) * a.out_ld + col;
-            const int32_t* sp = a.sorted_pair + r0 + hr;
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
                 if (i >= mt_act) continue;
@@ -528,7 +537,7 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
                 for (int r = 0; r < 16; ++r) {
                     const int c = i * 32 + 8 * (r >> 2) + (r & 3);
                     if (hr >= rows - c) continue;
-                    const float wgt = badtab ? __builtin_nanf("") : a.topk_w[sp[c]];
+                    const float wgt = badtab ? __builtin_nanf("") : s_roww[hr + c];
 #pragma unroll
                     for (int j = 0; j < NT; ++j)
                         if (col + 32 * j < N) ob[(size_t)c * a.out_ld + 32 * j] = wgt * acc[i][j][r];
