@@ -2,7 +2,8 @@
 // projection) are summed in fixed slot order in fp32, the optional residual is added, and the
 // row is rounded to bf16 (README of GLM-5.2-EXL3-TR3v4-3.5bpw-MTP78, "Shared residual
 // rotations": expert outputs are routing-weighted and summed back into the residual space).
-// One workgroup per (token, 1024-column chunk), flattened into one grid dimension; 16-byte loads of yp, 8-byte stores of y.
+// One workgroup per (token, 1024-column chunk), flattened into one grid dimension; 16-byte loads
+// of yp, 8-byte stores of y.
 #include "moeq_device.h"
 
 namespace moeq {
@@ -19,11 +20,20 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     const int valid = offsets[E];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     bool bad = false;
-    for (int j = 0; j < k; ++j) {
-        const int pos = pair_pos[(size_t)t * k + j];
-        if (pos >= valid) { bad = true; continue; }
-        const float4 v = *reinterpret_cast<const float4*>(yp + (size_t)pos * H + h);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    // the k rows' loads go out back to back (no branch around a load: an invalid position
+    // reads row 0 and only marks the result); yp is read once, hence non-temporal
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int pos = j0 + j < k ? pair_pos[(size_t)t * k + j0 + j] : 0;
+            bad |= j0 + j < k && pos >= valid;
+            pos = pos < valid ? pos : 0;
+            v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yp + (size_t)pos * H + h));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j0 + j < k) { acc.x += v[j][0]; acc.y += v[j][1]; acc.z += v[j][2]; acc.w += v[j][3]; }
     }
     if (residual) {
         const uint2 r = *reinterpret_cast<const uint2*>(residual + (size_t)t * H + h);
