@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--copies", type=int, default=4,
                     help="device copies of the weights rotated over the steps (MALL-cold reads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -105,6 +105,116 @@ def cpu_baseline(cfg, lw, x, logits, n_tokens):
                       f"(BLAS threads {threads}, os.cpu_count {os.cpu_count()})"}
 
 
+def run_stack(args, cfg):
+    """The 32-layer stack decode (64 tokens): one step = the forward through every layer, the
+    MoE output added to X in place. The layers' codes and scales are drawn on the device
+    (uniform code bytes, scale bytes 119..123, i.e. the magnitude of N(0, 0.01..0.02) weights):
+    the kernels' work does not depend on the weight values, and generating 32 distinct 5.1 GB
+    layers on the host would take many minutes (their parity is checked against the oracle by
+    the stack tests). Tables: each layer's own fitted grid and E2M1; router logits N(0, 1) per
+    layer, as the workload defines them."""
+    import torch
+    import codebook_quantized_moe_amd as mq
+    import synth
+
+    T, H, I, E, k, L = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.layers
+    dev = torch.device("cuda")
+    t_gen = time.perf_counter()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.key(cfg.cfg_id, 99))
+
+    def codes(N, K):
+        return torch.randint(0, 256, (E, N, K // 2), dtype=torch.uint8, device=dev, generator=gen)
+
+    def scales(N, K):
+        return torch.randint(119, 124, (E, N, K // 32), dtype=torch.uint8, device=dev,
+                             generator=gen)
+
+    layers = []
+    for l in range(L):
+        tables = np.stack([synth.lloyd_grid(cfg.cfg_id, l), synth.E2M1_GRID]).astype(np.float32)
+        w = mq.DeviceWeights(codes(I, H), scales(I, H), codes(I, H), scales(I, H), codes(H, I),
+                             scales(H, I), tables, torch.zeros(E, dtype=torch.uint8, device=dev))
+        lg = torch.from_numpy(synth.make_logits(cfg.cfg_id, T, E, layer=l)).to(dev)
+        layers.append((w, lg))
+        print(f"stack layer {l} on the device", file=sys.stderr, flush=True)
+    x0 = torch.from_numpy(synth.make_x(cfg.cfg_id, T, H).view(np.int16)).to(dev)
+    X = torch.empty_like(x0)
+    ML = mq.MoeLayer(T, H, I, E, k)
+    touched = []
+    for w, lg in layers:
+        ML.route(lg)
+        ML.permute()
+        touched.append(int((np.diff(ML.offsets.cpu().numpy()) > 0).sum()))
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+
+    nb = args.warmup + args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(L)] for _ in range(nb)]
+
+    def step(b):
+        X.copy_(x0)
+        for l, (w, lg) in enumerate(layers):
+            ML.route(lg)
+            ML.permute()
+            ev[b][l][0].record()
+            ML.gateup(X, w)
+            ev[b][l][1].record()
+            ML.down(w)
+            ML.combine(residual=X, out=X)
+
+    for b in range(args.warmup):
+        step(b)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for b in range(args.warmup, nb):
+        step(b)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+    value = T * args.steps / (total_ms / 1e3)
+    gu_w, dn_w = expert_bytes(H, I)
+    P = T * k
+    gu_us = [ev[b][l][0].elapsed_time(ev[b][l][1]) * 1e3 for b in range(args.warmup, nb)
+             for l in range(L)]
+    gu_bytes = [touched[l] * gu_w + T * H * 2 + P * I * 2 for l in range(L)]
+    ach = float(np.mean(gu_bytes)) / (float(np.mean(gu_us)) / 1e6) / 1e9
+    step_bytes = sum(touched[l] * (gu_w + dn_w) for l in range(L)) + L * (T * E * 4 + 3 * T * H * 2)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (codes and scales drawn on the device)",
+        "config": {"workload": cfg.name, "tokens": T, "hidden": H, "intermediate": I,
+                   "experts": E, "top_k": k, "layers": L, "residual": True},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic("decode_kernel<true>", cfg.name),
+                     "kernel": "decode_kernel<true>",
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, profiles/)"},
+        "stack": {"touched_experts_avg": round(float(np.mean(touched)), 2),
+                  "algorithmic_bytes_per_step": int(step_bytes),
+                  "step_GB_s": round(step_bytes / ms_per_step / 1e6, 1),
+                  "step_hbm_frac": round(step_bytes / ms_per_step / 1e6 / HBM_PEAK_GBS, 4),
+                  "gateup_avg_us": round(float(np.mean(gu_us)), 2)},
+        "input_setup_s": round(t_gen, 1),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -117,6 +227,8 @@ def main():
     import synth
 
     cfg = synth.CONFIGS[args.config]
+    if cfg.layers > 1:
+        return run_stack(args, cfg)
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     dev = torch.device("cuda")
     t_gen = time.perf_counter()
