@@ -18,10 +18,16 @@ Sources (the pages' titles; the section named on each function):
   permutation of gate-N, up-N and down-K is exact because SwiGLU is elementwise).
 * [readme] README of GLM-5.2-EXL3-TR3v4-3.5bpw-MTP78, "What had to be fixed" / "Shared
   residual rotations": expert outputs are router-weighted and summed back per token.
+* [dense6] GLM-5.2-EXL3-DENSE6-MTP78 model card, "Quant recipe": the router (mlp.gate) is held
+  in BF16; [brief] "Target pipeline": a layer's routing is the router applied to its
+  activations.
 
 Readings where the pages are silent (each is listed with its reason in the design notes):
 
-* gating: softmax over the k selected logits (textbook top-k gating);
+* gating: softmax over the k selected logits (textbook top-k gating), or the logistic
+  sigmoid of each selected logit renormalised over the k (the other textbook form); either
+  way the k experts are the k largest logits (the sigmoid is increasing);
+* router logits: the plain product of the bf16 activations and the bf16 router rows;
 * top-k order: IEEE-754 totalOrder on the fp32 logit bits, descending, ties (identical
   bits) to the lower expert id;
 * permutation: pairs p = t*k + j sorted by (expert, p), i.e. a stable sort; pairs whose id
@@ -36,7 +42,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "bf16_to_f64", "rne_bf16", "total_order_key", "route_topk", "permute_by_expert",
+    "bf16_to_f64", "rne_bf16", "total_order_key", "router_logits", "route_topk",
+    "permute_by_expert",
     "unpack_codes", "dequant_bf16", "layer_forward", "stack_forward", "E2M1_TABLE",
 ]
 
@@ -107,14 +114,29 @@ def total_order_key(logits) -> np.ndarray:
     return np.where(neg, ~b, b | np.uint32(0x80000000)).astype(np.uint32)
 
 
-def route_topk(logits, k: int):
+def router_logits(x_bits, router_bits) -> np.ndarray:
+    """Router logits l[t, e] = sum_h x[t, h] * Wr[e, h] over the bf16 values, in fp64.
+
+    [dense6] "Quant recipe": the router weight is kept in BF16; [brief] "Target pipeline":
+    routing_L = router(acts_L). x_bits uint16 [T, H], router_bits uint16 [E, H].
+    Returns float64 [T, E].
+    """
+    x = bf16_to_f64(x_bits)
+    wr = bf16_to_f64(router_bits)
+    return x @ wr.T
+
+
+def route_topk(logits, k: int, gating: str = "softmax"):
     """Top-k experts per token and their gate values.
 
     [brief] model geometry: each token selects 8 of 256 routed experts. Order of the k ids:
-    logit descending (totalOrder), ties to the lower expert id. Gate values: softmax over
-    the k selected logits, w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), in fp64.
+    logit descending (totalOrder), ties to the lower expert id. Gate values, in fp64, over
+    the k selected logits: "softmax", w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0); or
+    "sigmoid", s_j = 1 / (1 + exp(-l_j)) and w_j = s_j / sum_i s_i.
     Returns ids int32 [T, k], w float64 [T, k].
     """
+    if gating not in ("softmax", "sigmoid"):
+        raise ValueError(gating)
     logits = np.ascontiguousarray(logits, dtype=np.float32)
     T, E = logits.shape
     assert 1 <= k <= E
@@ -127,8 +149,12 @@ def route_topk(logits, k: int):
         sel = order[:k]
         ids[t] = sel
         lv = logits[t, sel].astype(np.float64)
-        ex = np.exp(lv - lv[0])
-        w[t] = ex / ex.sum()
+        if gating == "softmax":
+            ex = np.exp(lv - lv[0])
+            w[t] = ex / ex.sum()
+        else:
+            sg = 1.0 / (1.0 + np.exp(-lv))
+            w[t] = sg / sg.sum()
     return ids, w
 
 

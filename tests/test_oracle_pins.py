@@ -174,6 +174,70 @@ def test_topk_gate_weights_match_mixtral_router():
     np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-14)
 
 
+def test_sigmoid_gate_closed_forms():
+    """Sigmoid gating: the k largest logits, s_j = 1/(1 + exp(-l_j)), renormalised."""
+    # selected logits (x, -x): s = (sigmoid(x), 1 - sigmoid(x)) already sums to 1
+    x = 0.7
+    ids, w = oracle.route_topk(np.array([[x, -3.0, -x, -5.0]], np.float32), 2, gating="sigmoid")
+    assert ids.tolist() == [[0, 2]]
+    xf = float(np.float32(x))
+    np.testing.assert_allclose(w[0], [1 / (1 + np.exp(-xf)), 1 / (1 + np.exp(xf))], rtol=1e-15)
+    # logits (ln 3, 0): s = (3/4, 1/2) -> w = (0.6, 0.4)
+    l3 = np.float32(np.log(3.0))
+    _, w = oracle.route_topk(np.array([[0.0, l3, -1.0]], np.float32), 2, gating="sigmoid")
+    s3 = 1 / (1 + np.exp(-float(l3)))
+    np.testing.assert_allclose(w[0], [s3 / (s3 + 0.5), 0.5 / (s3 + 0.5)], rtol=1e-15)
+    np.testing.assert_allclose(w[0], [0.6, 0.4], rtol=1e-7)
+    # equal logits: uniform weights; the same experts as softmax gating
+    _, w = oracle.route_topk(np.full((1, 8), 0.25, np.float32), 4, gating="sigmoid")
+    np.testing.assert_allclose(w, 0.25, rtol=1e-15)
+    g = np.random.default_rng(4)
+    logits = g.standard_normal((6, 64)).astype(np.float32)
+    i1, _ = oracle.route_topk(logits, 8)
+    i2, w2 = oracle.route_topk(logits, 8, gating="sigmoid")
+    np.testing.assert_array_equal(i1, i2)
+    np.testing.assert_allclose(w2.sum(1), 1.0, rtol=1e-14)
+
+
+def test_router_logits_closed_forms():
+    """Router logits are the plain product of bf16 activations and bf16 router rows."""
+    T, H, E = 3, 64, 5
+    one = oracle.rne_bf16(np.ones((T, H)))
+    rows = oracle.rne_bf16(np.arange(E, dtype=np.float64)[:, None] * np.ones((1, H)))
+    np.testing.assert_array_equal(oracle.router_logits(one, rows), np.arange(E)[None, :] * H * np.ones((T, 1)))
+    # a one-hot activation row picks one column of the router
+    g = np.random.default_rng(8)
+    wr = oracle.rne_bf16(g.standard_normal((E, H)))
+    x = np.zeros((1, H))
+    x[0, 17] = 1.0
+    np.testing.assert_array_equal(oracle.router_logits(oracle.rne_bf16(x), wr)[0],
+                                  oracle.bf16_to_f64(wr)[:, 17])
+
+
+def test_router_and_sigmoid_gate_match_glm4_moe_router():
+    """Against transformers' GLM-4.5 MoE router with one group, no score bias, renormalised
+    top-k and scaling 1: logits (fp32 there), expert sets and gate weights."""
+    from transformers import Glm4MoeConfig
+    from transformers.models.glm4_moe.modeling_glm4_moe import Glm4MoeTopkRouter
+    g = np.random.default_rng(5)
+    T, H, E, k = 12, 128, 256, 8
+    x = oracle.rne_bf16(g.standard_normal((T, H)))
+    wr = oracle.rne_bf16(0.1 * g.standard_normal((E, H)))
+    logits = oracle.router_logits(x, wr)
+    ids, w = oracle.route_topk(logits.astype(np.float32), k, gating="sigmoid")
+    cfg = Glm4MoeConfig(hidden_size=H, n_routed_experts=E, num_experts_per_tok=k, n_group=1,
+                        topk_group=1, norm_topk_prob=True, routed_scaling_factor=1.0)
+    r = Glm4MoeTopkRouter(cfg)
+    with torch.no_grad():
+        r.weight.copy_(torch.from_numpy(oracle.bf16_to_f64(wr)).float())
+        rl, tw, ti = r(torch.from_numpy(oracle.bf16_to_f64(x)).float())
+    np.testing.assert_allclose(logits, rl.double().numpy(), rtol=1e-5, atol=1e-5)
+    for t in range(T):
+        ref = dict(zip(ti[t].tolist(), tw[t].double().tolist()))
+        assert sorted(ref) == sorted(ids[t].tolist())
+        np.testing.assert_allclose(w[t], [ref[e] for e in ids[t]], rtol=2e-6, atol=1e-7)
+
+
 def test_topk_ties_and_signed_zero():
     logits = np.array([[1.0, 3.0, 3.0, -0.0, 0.0, 3.0]], np.float32)
     ids, w = oracle.route_topk(logits, 5)
