@@ -26,11 +26,11 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 MOEQ_OK, MOEQ_EINVAL, MOEQ_EUNSUPPORTED, MOEQ_EWORKSPACE, MOEQ_ELAUNCH = 0, -1, -2, -3, -4
-MOEQ_GATING_SOFTMAX_TOPK = 0
+MOEQ_GATING_SOFTMAX_TOPK, MOEQ_GATING_SIGMOID_TOPK = 0, 1
 MAX_EXPERTS = 256
 MAX_TABLES = 4
 
-EXPORTED = ("moeq_last_error", "moeq_workspace_bytes", "moeq_route_topk",
+EXPORTED = ("moeq_last_error", "moeq_workspace_bytes", "moeq_router_logits", "moeq_route_topk",
             "moeq_permute_by_expert", "moeq_gateup_swiglu", "moeq_down",
             "moeq_unpermute_combine", "moeq_debug_dequant")
 
@@ -39,6 +39,8 @@ _lib.moeq_last_error.restype = ctypes.c_char_p
 _lib.moeq_last_error.argtypes = []
 _lib.moeq_workspace_bytes.restype = _sz
 _lib.moeq_workspace_bytes.argtypes = [_i] * 5
+_lib.moeq_router_logits.restype = _i
+_lib.moeq_router_logits.argtypes = [_vp, _i, _i, _vp, _i, _vp, _vp]
 _lib.moeq_route_topk.restype = _i
 _lib.moeq_route_topk.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp, _vp]
 _lib.moeq_permute_by_expert.restype = _i
@@ -99,6 +101,10 @@ def moeq_last_error() -> str:
 
 def moeq_workspace_bytes(T: int, k: int, E: int, H: int, I: int) -> int:
     return int(_lib.moeq_workspace_bytes(T, k, E, H, I))
+
+
+def moeq_router_logits(x, T, H, router_w, E, logits, stream=None):
+    _check(_lib.moeq_router_logits(_p(x), T, H, _p(router_w), E, _p(logits), _stream(stream)))
 
 
 def moeq_route_topk(logits, T, E, k, topk_ids, topk_w, gating=MOEQ_GATING_SOFTMAX_TOPK,

@@ -129,15 +129,34 @@ size_t moeq_workspace_bytes(int T, int k, int E, int H, int I) {
     return prefill_queue_bytes() + prefill_split_bytes(T, H);
 }
 
+int moeq_router_logits(const uint16_t* x, int T, int H, const uint16_t* router_w, int E,
+                       float* logits, void* stream) {
+    const char* w = "moeq_router_logits";
+    if (T < 0 || H <= 0 || E < 1 || E > MOEQ_MAX_EXPERTS)
+        return fail(MOEQ_EINVAL, "%s: bad sizes T=%d H=%d E=%d", w, T, H, E);
+    if (H % 64 != 0) return fail(MOEQ_EUNSUPPORTED, "%s: H=%d must be a multiple of 64", w, H);
+    if ((long long)T * H * 2 >= (1LL << 31) || (long long)E * H * 2 >= (1LL << 31))
+        return fail(MOEQ_EUNSUPPORTED, "%s: x and router_w must be under 2 GiB (T=%d, H=%d)", w, T, H);
+    if (T == 0) return ok();
+    if (!x || !router_w || !logits) return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(logits, 4))
+        return fail(MOEQ_EUNSUPPORTED, "%s: x and router_w must be 16-byte aligned, logits 4-byte aligned", w);
+    clear_hip_error();
+    launch_router_logits(x, T, H, router_w, E, logits, (hipStream_t)stream);
+    return check_launch(w);
+}
+
 int moeq_route_topk(const float* logits, int T, int E, int k, int gating, int32_t* topk_ids,
                     float* topk_w, void* stream) {
     const char* w = "moeq_route_topk";
     if (int r = check_sizes(w, T, k, E)) return r;
-    if (gating != MOEQ_GATING_SOFTMAX_TOPK) return fail(MOEQ_EINVAL, "%s: unknown gating %d", w, gating);
+    if (gating != MOEQ_GATING_SOFTMAX_TOPK && gating != MOEQ_GATING_SIGMOID_TOPK)
+        return fail(MOEQ_EINVAL, "%s: unknown gating %d", w, gating);
     if (T == 0) return ok();
     if (!logits || !topk_ids || !topk_w) return fail(MOEQ_EINVAL, "%s: null pointer", w);
     clear_hip_error();
-    launch_route_topk(logits, T, E, k, topk_ids, topk_w, (hipStream_t)stream);
+    launch_route_topk(logits, T, E, k, gating == MOEQ_GATING_SIGMOID_TOPK, topk_ids, topk_w,
+                      (hipStream_t)stream);
     return check_launch(w);
 }
 

@@ -28,8 +28,10 @@ struct SkinnyArgs {
     TableArgs tables;
 };
 
-void launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                       hipStream_t stream);
+void launch_router_logits(const uint16_t* x, int T, int H, const uint16_t* wr, int E,
+                          float* logits, hipStream_t stream);
+void launch_route_topk(const float* logits, int T, int E, int k, bool sigmoid, int32_t* ids,
+                       float* w, hipStream_t stream);
 void launch_permute(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pair,
                     int32_t* pair_pos, hipStream_t stream);
 void launch_decode(const SkinnyArgs& a, bool gateup, long tiles, int cus, int shape,

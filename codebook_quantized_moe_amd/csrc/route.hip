@@ -13,15 +13,35 @@ __device__ __forceinline__ uint32_t total_order_key(float f) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// One DPP step of a max reduction: each lane takes the larger of its key and the key that the
+// DPP pattern CTRL brings from another lane of its row of 16.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t read_lane_u64(uint64_t v, int lane) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Wave-wide maximum of a 64-bit key, the same value in every lane: the maximum of each row of
+// 16 lanes with DPP moves (swap neighbours, swap pairs, rotate the row by 4, then by 8), then
+// the four row maxima through scalar registers. DPP steps are plain VALU operations, where a
+// lane shuffle would go through the LDS crossbar with its longer latency.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+    v = dpp_max_step<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v = dpp_max_step<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v = dpp_max_step<0x124>(v);   // row_ror 4
+    v = dpp_max_step<0x128>(v);   // row_ror 8
+    const uint64_t r0 = read_lane_u64(v, 0), r1 = read_lane_u64(v, 16);
+    const uint64_t r2 = read_lane_u64(v, 32), r3 = read_lane_u64(v, 48);
+    const uint64_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+    return a > b ? a : b;
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
@@ -31,7 +51,8 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 }
 
 __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits, int T,
-                                                         int E, int k, int32_t* __restrict__ ids,
+                                                         int E, int k, int sigmoid,
+                                                         int32_t* __restrict__ ids,
                                                          float* __restrict__ w) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -69,7 +90,21 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
     float ex[4], part = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        ex[j] = (64 * j + lane < k) ? expf(my_val[j] - l0) : 0.0f;
+        const float l = my_val[j];
+        float s;
+        if (!sigmoid) {
+            s = expf(l - l0);
+        } else if (l0 < 0.0f) {
+            // every selected logit is negative: sigmoid(l) = e^l / (1 + e^l); the common
+            // factor e^l0 is taken out so no term underflows and slot 0 contributes >= 1/2
+            s = expf(l - l0) / (1.0f + expf(l));
+        } else if (l >= 0.0f) {
+            s = 1.0f / (1.0f + expf(-l));
+        } else {
+            const float e = expf(l);
+            s = e / (1.0f + e);
+        }
+        ex[j] = (64 * j + lane < k) ? s : 0.0f;
         part += ex[j];
     }
     const float sum = wave_sum_f32(part);
@@ -83,11 +118,11 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
     }
 }
 
-void launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                       hipStream_t stream) {
+void launch_route_topk(const float* logits, int T, int E, int k, bool sigmoid, int32_t* ids,
+                       float* w, hipStream_t stream) {
     const int blocks = (T + 3) / 4;
     hipLaunchKernelGGL(route_topk_kernel, dim3(blocks), dim3(256), 0, stream, logits, T, E, k,
-                       ids, w);
+                       sigmoid ? 1 : 0, ids, w);
 }
 
 }  // namespace moeq

@@ -1,8 +1,8 @@
-"""Buffers and call sequence of one routed-MoE layer forward over libmoeq's five calls.
+"""Buffers and call sequence of one routed-MoE layer forward over libmoeq's calls.
 
 Plumbing only: torch allocates the device buffers once; ``forward`` enqueues
 route -> permute -> gate|up+SwiGLU -> down -> unpermute/combine on one stream with no
-host synchronisation in between.
+host synchronisation in between; ``forward_routed`` puts the bf16 router in front.
 """
 from __future__ import annotations
 
@@ -11,8 +11,8 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from . import (moeq_down, moeq_gateup_swiglu, moeq_permute_by_expert, moeq_route_topk,
-               moeq_unpermute_combine, moeq_workspace_bytes)
+from . import (MOEQ_GATING_SOFTMAX_TOPK, moeq_down, moeq_gateup_swiglu, moeq_permute_by_expert,
+               moeq_route_topk, moeq_router_logits, moeq_unpermute_combine, moeq_workspace_bytes)
 
 
 @dataclass
@@ -51,10 +51,13 @@ class DeviceWeights:
 class MoeLayer:
     """Preallocated buffers for T tokens of a layer with E experts, top-k."""
 
-    def __init__(self, T: int, H: int, I: int, E: int, k: int, device="cuda"):
+    def __init__(self, T: int, H: int, I: int, E: int, k: int, device="cuda",
+                 gating: int = MOEQ_GATING_SOFTMAX_TOPK):
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
+        self.gating = gating
         P = T * k
         i32 = dict(dtype=torch.int32, device=device)
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=device)
         self.topk_ids = torch.empty(P, **i32)
         self.topk_w = torch.empty(P, dtype=torch.float32, device=device)
         self.offsets = torch.empty(E + 1, **i32)
@@ -66,8 +69,14 @@ class MoeLayer:
         self.ws_bytes = moeq_workspace_bytes(T, k, E, H, I)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
 
+    def router(self, x, router_w, stream=None):
+        """x: bf16 bits [T, H]; router_w: bf16 bits [E, H]. Writes and returns self.logits."""
+        moeq_router_logits(x, self.T, self.H, router_w, self.E, self.logits, stream=stream)
+        return self.logits
+
     def route(self, logits, stream=None):
-        moeq_route_topk(logits, self.T, self.E, self.k, self.topk_ids, self.topk_w, stream=stream)
+        moeq_route_topk(logits, self.T, self.E, self.k, self.topk_ids, self.topk_w,
+                        gating=self.gating, stream=stream)
 
     def permute(self, stream=None):
         moeq_permute_by_expert(self.topk_ids, self.T, self.k, self.E, self.offsets,
@@ -93,6 +102,16 @@ class MoeLayer:
     def forward(self, x, logits, w: DeviceWeights, residual=None, out=None, stream=None):
         """x: int16 (bf16 bits) [T, H] cuda; logits fp32 [T, E] cuda. Returns y (bf16 bits)."""
         self.route(logits, stream)
+        self.permute(stream)
+        self.gateup(x, w, stream)
+        self.down(w, stream)
+        return self.combine(residual, out, stream)
+
+    def forward_routed(self, x, router_w, w: DeviceWeights, residual=None, out=None,
+                       stream=None):
+        """As forward, with the logits computed from x by the bf16 router router_w [E, H]."""
+        self.router(x, router_w, stream)
+        self.route(self.logits, stream)
         self.permute(stream)
         self.gateup(x, w, stream)
         self.down(w, stream)

@@ -54,10 +54,14 @@ enum moeq_status {
     MOEQ_ELAUNCH = -4        /* a HIP launch reported an error */
 };
 
-/* Gate scoring. Only softmax over the k selected logits is defined: the pages say expert
- * outputs are router-weighted but not how the weights are formed; this is textbook top-k
- * gating (softmax of the kept logits). */
-enum moeq_gating { MOEQ_GATING_SOFTMAX_TOPK = 0 };
+/* Gate scoring. The pages say expert outputs are router-weighted but not how the weights are
+ * formed, so two textbook forms are offered; both select the same k experts (the largest
+ * logits: sigmoid is increasing).
+ *   MOEQ_GATING_SOFTMAX_TOPK  softmax over the k selected logits
+ *   MOEQ_GATING_SIGMOID_TOPK  sigmoid of each selected logit, divided by their sum (the
+ *                             scoring of GLM-4.5-family routers, without the bias term and
+ *                             group limit, which the pages do not mention) */
+enum moeq_gating { MOEQ_GATING_SOFTMAX_TOPK = 0, MOEQ_GATING_SIGMOID_TOPK = 1 };
 
 #define MOEQ_MAX_EXPERTS 256
 #define MOEQ_MAX_TABLES 4
@@ -81,10 +85,28 @@ const char* moeq_last_error(void);
 size_t moeq_workspace_bytes(int T, int k, int E, int H, int I);
 
 /*
+ * Router logits: logits[t, e] = sum_h x[t, h] * router_w[e, h], products of bf16 values summed
+ * in fp32 (GLM-5.2-EXL3-DENSE6-MTP78 model card, "Quant recipe": the router stays in BF16;
+ * "Round 7" brief, "Target pipeline": the routing of a layer is its router applied to the
+ * layer's activations). The summation order is fixed (the same bits on every call), not the
+ * order of a sequential sum.
+ *   x         bf16 [T, H]  in, row-major, 16-byte aligned
+ *   router_w  bf16 [E, H]  in, row-major (one row per expert), 16-byte aligned
+ *   logits    fp32 [T, E]  out, row-major, 4-byte aligned
+ * T = 0 is a no-op. Errors: MOEQ_EINVAL for null pointers, T < 0, H <= 0, E outside [1, 256];
+ * MOEQ_EUNSUPPORTED when H is not a multiple of 64, x or router_w is 2 GiB or more, or a
+ * pointer is misaligned. The caller owns every buffer; nothing is allocated.
+ */
+int moeq_router_logits(const uint16_t* x, int T, int H, const uint16_t* router_w, int E,
+                       float* logits, void* stream);
+
+/*
  * Top-k routing. For each token t, topk_ids[t, 0..k) are the k experts with the largest
  * logits, in descending logit order under IEEE-754 totalOrder of the fp32 bit patterns;
- * equal bit patterns go to the lower expert id. topk_w[t, j] = softmax over the k selected
- * logits (fp32), w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0). The gate values are finite
+ * equal bit patterns go to the lower expert id. topk_w[t, j] (fp32) is, for
+ * MOEQ_GATING_SOFTMAX_TOPK, w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected
+ * logits, and for MOEQ_GATING_SIGMOID_TOPK, w_j = s_j / sum_i s_i with s = sigmoid(l),
+ * evaluated so that no term overflows or all of them underflow. The gate values are finite
  * when the selected logits are. (Source for top-8 of 256: "Round 7" brief, Model geometry.)
  *   logits   fp32 [T, E]   in
  *   topk_ids int32 [T, k]  out

@@ -42,7 +42,7 @@ E2M1_DEFECT_EXPERTS = (164, 86, 15, 30, 139)
 WEIGHT_SIGMA = 0.02
 
 # seed streams
-S_X, S_LOGITS, S_ZIPF, S_LLOYD, S_WEIGHTS, S_PERM = 0, 1, 2, 3, 4, 5
+S_X, S_LOGITS, S_ZIPF, S_LLOYD, S_WEIGHTS, S_PERM, S_ROUTER = 0, 1, 2, 3, 4, 5, 6
 
 
 def build_lib(force: bool = False) -> str:
@@ -113,6 +113,13 @@ def make_x(cfg_id: int, T: int, H: int, layer: int = 0, batch: int = 0) -> np.nd
     """bf16 bits [T, H] from N(0, 1)."""
     x = rng(cfg_id, S_X, layer, batch).standard_normal((T, H), dtype=np.float32)
     return bf16_bits_from_f32(x)
+
+
+def make_router(cfg_id: int, E: int, H: int, layer: int = 0) -> np.ndarray:
+    """bf16 bits [E, H] of a router weight drawn from N(0, 1/H), so that with x from make_x
+    the logits are about N(0, 1)."""
+    w = rng(cfg_id, S_ROUTER, layer).standard_normal((E, H), dtype=np.float32)
+    return bf16_bits_from_f32(w / np.float32(np.sqrt(H)))
 
 
 def zipf_bias(cfg_id: int, E: int, s: float, layer: int = 0) -> np.ndarray:

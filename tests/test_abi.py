@@ -56,6 +56,27 @@ def test_route_validation():
     mq.moeq_route_topk(None, 0, 256, 8, None, None, stream=0)       # T = 0: no-op, OK
 
 
+def test_router_validation():
+    f = mq.moeq_router_logits
+    assert _status(f, FAKE, 4, 0, FAKE, 256, FAKE, stream=0) == mq.MOEQ_EINVAL      # H <= 0
+    assert _status(f, FAKE, -1, 64, FAKE, 256, FAKE, stream=0) == mq.MOEQ_EINVAL    # T < 0
+    assert _status(f, FAKE, 4, 64, FAKE, 0, FAKE, stream=0) == mq.MOEQ_EINVAL       # E < 1
+    assert _status(f, FAKE, 4, 64, FAKE, 257, FAKE, stream=0) == mq.MOEQ_EINVAL     # E > 256
+    assert _status(f, FAKE, 4, 96, FAKE, 256, FAKE, stream=0) == mq.MOEQ_EUNSUPPORTED
+    assert "multiple of 64" in mq.moeq_last_error()
+    assert _status(f, FAKE, 1 << 20, 1024, FAKE, 256, FAKE, stream=0) == mq.MOEQ_EUNSUPPORTED
+    assert _status(f, None, 4, 64, FAKE, 256, FAKE, stream=0) == mq.MOEQ_EINVAL
+    assert _status(f, FAKE, 4, 64, FAKE, 256, None, stream=0) == mq.MOEQ_EINVAL
+    assert _status(f, FAKE + 8, 4, 64, FAKE, 256, FAKE, stream=0) == mq.MOEQ_EUNSUPPORTED
+    assert _status(f, FAKE, 4, 64, FAKE, 256, FAKE + 2, stream=0) == mq.MOEQ_EUNSUPPORTED
+    f(None, 0, 64, None, 256, None, stream=0)                       # T = 0: no-op, OK
+    # the sigmoid gating is a known mode: a bad size still fails on the size, not the mode
+    assert _status(mq.moeq_route_topk, FAKE, 4, 8, 9, FAKE, FAKE,
+                   gating=mq.MOEQ_GATING_SIGMOID_TOPK, stream=0) == mq.MOEQ_EINVAL
+    assert "gating" not in mq.moeq_last_error()
+    mq.moeq_route_topk(None, 0, 256, 8, None, None, gating=mq.MOEQ_GATING_SIGMOID_TOPK, stream=0)
+
+
 def test_permute_validation():
     assert _status(mq.moeq_permute_by_expert, FAKE, 4, 8, 0, FAKE, FAKE, FAKE,
                    stream=0) == mq.MOEQ_EINVAL

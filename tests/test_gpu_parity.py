@@ -161,6 +161,101 @@ def test_route_ties_and_signed_zero():
     np.testing.assert_array_equal(host(ids).reshape(T, k), rid)
 
 
+@pytest.mark.parametrize("T,E,k,zipf", [(16, 4, 2, None), (8, 256, 8, None), (2048, 256, 8, 1.0),
+                                        (33, 64, 64, None), (1, 17, 1, None), (5, 256, 256, None)])
+def test_route_sigmoid_gating(T, E, k, zipf):
+    mq = _mq()
+    logits = synth.make_logits(8, T, E, zipf_s=zipf)
+    ids = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    mq.moeq_route_topk(dev(logits), T, E, k, ids, w, gating=mq.MOEQ_GATING_SIGMOID_TOPK)
+    rid, rw = oracle.route_topk(logits, k, "sigmoid")
+    np.testing.assert_array_equal(host(ids).reshape(T, k), rid)
+    np.testing.assert_allclose(host(w).reshape(T, k), rw, rtol=2e-6, atol=1e-7)
+
+
+def test_route_sigmoid_gating_extreme_logits():
+    """Selected logits far below zero (sigmoid underflows fp32 below about -104), straddling
+    the sign, and far above zero (sigmoid rounds to one): weights stay finite and exact."""
+    mq = _mq()
+    E, k = 64, 8
+    g = np.random.default_rng(5)
+    rows = [g.uniform(-300, -250, E), g.uniform(-110, -80, E), g.uniform(-4, 4, E),
+            g.uniform(60, 90, E), np.concatenate([g.uniform(-95, -90, E - 1), [0.5]]),
+            np.concatenate([g.uniform(-300, -200, E - 2), [-1e-30, 1e-30]])]
+    logits = np.array(rows, np.float32)
+    T = logits.shape[0]
+    ids = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    mq.moeq_route_topk(dev(logits), T, E, k, ids, w, gating=mq.MOEQ_GATING_SIGMOID_TOPK)
+    rid, rw = oracle.route_topk(logits, k, "sigmoid")
+    gw = host(w).reshape(T, k)
+    np.testing.assert_array_equal(host(ids).reshape(T, k), rid)
+    assert np.all(np.isfinite(gw))
+    np.testing.assert_allclose(gw, rw, rtol=2e-6, atol=1e-7)
+
+
+def _router_case(seed, T, H, E):
+    x = synth.make_x(seed, T, H)
+    wr = synth.make_router(seed, E, H)
+    return x, wr
+
+
+def _router_bound(x, wr):
+    """Rounding bound of an fp32 sum of exact bf16 products in which a term meets at most
+    n = H/16 + 8 roundings (one per 16-wide MFMA step of the longest chain, plus the adds
+    inside an MFMA and between wavefronts): n * 2^-24 * sum_h |x_h w_h| (|.| by clearing the
+    sign bits)."""
+    n = x.shape[1] // 16 + 8
+    ax = (x & np.uint16(0x7FFF)).astype(np.uint16)
+    aw = (wr & np.uint16(0x7FFF)).astype(np.uint16)
+    return n * 2.0 ** -24 * oracle.router_logits(ax, aw)
+
+
+@pytest.mark.parametrize("T,H,E", [(8, 6144, 256),      # decode batch: few-tokens kernel, K / 16
+                                   (37, 576, 17),       # ragged tokens and experts, K / 2
+                                   (1, 64, 1),          # one token, one expert, one K step
+                                   (64, 640, 256),      # last few-tokens size, K / 4
+                                   (65, 1024, 48),      # first many-tokens size
+                                   (100, 1088, 200),    # K groups with a ragged last group
+                                   (2048, 6144, 256)])  # prefill batch
+def test_router_logits(T, H, E):
+    mq = _mq()
+    x, wr = _router_case(31, T, H, E)
+    logits = torch.full((T, E), float("nan"), dtype=torch.float32, device="cuda")
+    mq.moeq_router_logits(dev(x.view(np.int16)), T, H, dev(wr.view(np.int16)), E, logits)
+    got = host(logits)
+    rows = np.arange(T) if T <= 256 else np.unique(np.r_[0, T - 1, np.arange(0, T, 61)])
+    ref = oracle.router_logits(x[rows], wr)
+    bound = _router_bound(x[rows], wr)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got[rows].astype(np.float64) - ref)
+    assert np.all(err <= bound), float((err / bound).max())
+    again = torch.empty_like(logits)
+    mq.moeq_router_logits(dev(x.view(np.int16)), T, H, dev(wr.view(np.int16)), E, again)
+    np.testing.assert_array_equal(host(again).view(np.uint32), got.view(np.uint32))
+
+
+def test_layer_routed_sigmoid(path):
+    """Router -> sigmoid top-k -> the expert path, all on the GPU; the selection and gates are
+    checked by applying the oracle's routing to the GPU's fp32 logits."""
+    mq = _mq()
+    T, E, H, I, k = 37, 8, 576, 320, 4
+    lw, x, _ = _case(27, T, E, H, I, k, e2m1_experts=(1,), permute="random")
+    wr = synth.make_router(27, E, H)
+    w = mq.DeviceWeights.from_host(lw)
+    L = mq.MoeLayer(T, H, I, E, k, gating=mq.MOEQ_GATING_SIGMOID_TOPK)
+    y = L.forward_routed(dev(x.view(np.int16)), dev(wr.view(np.int16)), w)
+    out = dict(ids=host(L.topk_ids).reshape(T, k), w=host(L.topk_w).reshape(T, k),
+               offsets=host(L.offsets), sorted_pair=host(L.sorted_pair),
+               pair_pos=host(L.pair_pos), inter=u16(L.inter), y=u16(y))
+    gl = host(L.logits)
+    assert np.all(np.abs(gl - oracle.router_logits(x, wr)) <= _router_bound(x, wr))
+    routing = oracle.route_topk(gl, k, "sigmoid")
+    ref = oracle.layer_forward(x, gl, k, lw, routing=routing)
+    check_layer(out, ref, k)
+
+
 @pytest.mark.parametrize("T,k,E", [(16, 2, 4), (8, 8, 256), (2048, 8, 256), (8192, 8, 256),
                                    (1, 1, 1), (129, 3, 7)])
 def test_permute_bitexact(T, k, E):

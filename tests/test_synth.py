@@ -138,3 +138,13 @@ def test_logits_zipf_skew():
     assert np.sort(c2)[::-1][:8].sum() / c2.sum() < 0.1
     for t in range(0, T, 97):
         assert len(np.unique(lg[t])) == E
+
+
+def test_router_weights_seeded_and_scaled():
+    H, E = 6144, 256
+    a = synth.make_router(4, E, H)
+    np.testing.assert_array_equal(a, synth.make_router(4, E, H))
+    assert not np.array_equal(a, synth.make_router(4, E, H, layer=1))
+    assert a.dtype == np.uint16 and a.shape == (E, H)
+    lg = oracle.router_logits(synth.make_x(4, 64, H), a)
+    assert 0.9 < lg.std() < 1.1          # logits about N(0, 1) with x ~ N(0, 1)
