@@ -10,7 +10,9 @@ weights that the previous steps left in the ~256 MB last-level cache (MALL).
 
 Prints ONE JSON line. ``roofline`` covers the dominant kernel (the fused gate|up projection):
 algorithmic bytes (touched experts' gate+up codes and scales + activations in/out) per launch
-divided by its average launch time, measured with HIP events on the launch stream.
+divided by its average launch time, measured with HIP events on the launch stream. The events
+sit in a second pass over the same timed batches: an event recorded between two kernels idles
+the GPU for about 5 us, so the pass that gives ``value`` has events only at its two ends.
 ``roofline.traffic`` is the kernel's HBM bytes per launch from the rocprofv3 counter summaries in
 ``profiles/`` (null when none matches the current kernel source).
 ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same workload.
@@ -52,6 +54,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2,
                     help="tokens of the workload the CPU oracle is timed on")
+    ap.add_argument("--router", action="store_true",
+                    help="stack: route every layer from its activations through a bf16 router "
+                         "(logits = X . Wr^T, sigmoid gating) instead of pre-drawn logits")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -112,7 +117,9 @@ def run_stack(args, cfg):
     the kernels' work does not depend on the weight values, and generating 32 distinct 5.1 GB
     layers on the host would take many minutes (their parity is checked against the oracle by
     the stack tests). Tables: each layer's own fitted grid and E2M1; router logits N(0, 1) per
-    layer, as the workload defines them."""
+    layer, as the workload defines them. With --router each layer instead routes from its own
+    activations: a bf16 router N(0, 1/H) per layer (logits about N(0, 1)), sigmoid gating, and
+    the router launch inside the step."""
     import torch
     import codebook_quantized_moe_amd as mq
     import synth
@@ -135,17 +142,35 @@ def run_stack(args, cfg):
         tables = np.stack([synth.lloyd_grid(cfg.cfg_id, l), synth.E2M1_GRID]).astype(np.float32)
         w = mq.DeviceWeights(codes(I, H), scales(I, H), codes(I, H), scales(I, H), codes(H, I),
                              scales(H, I), tables, torch.zeros(E, dtype=torch.uint8, device=dev))
-        lg = torch.from_numpy(synth.make_logits(cfg.cfg_id, T, E, layer=l)).to(dev)
-        layers.append((w, lg))
+        if args.router:
+            lg = torch.from_numpy(synth.make_router(cfg.cfg_id, E, H, layer=l).view(np.int16))
+        else:
+            lg = torch.from_numpy(synth.make_logits(cfg.cfg_id, T, E, layer=l))
+        layers.append((w, lg.to(dev)))
         print(f"stack layer {l} on the device", file=sys.stderr, flush=True)
     x0 = torch.from_numpy(synth.make_x(cfg.cfg_id, T, H).view(np.int16)).to(dev)
     X = torch.empty_like(x0)
-    ML = mq.MoeLayer(T, H, I, E, k)
+    ML = mq.MoeLayer(T, H, I, E, k, gating=(mq.MOEQ_GATING_SIGMOID_TOPK if args.router
+                                            else mq.MOEQ_GATING_SOFTMAX_TOPK))
+
+    def route(lg):
+        if args.router:
+            ML.router(X, lg)
+            ML.route(ML.logits)
+        else:
+            ML.route(lg)
+
+    # touched experts per layer (with the router they follow the activations, which every
+    # step starts again from x0, so one untimed pass gives them)
     touched = []
+    X.copy_(x0)
     for w, lg in layers:
-        ML.route(lg)
+        route(lg)
         ML.permute()
         touched.append(int((np.diff(ML.offsets.cpu().numpy()) > 0).sum()))
+        ML.gateup(X, w)
+        ML.down(w)
+        ML.combine(residual=X, out=X)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
 
@@ -153,17 +178,20 @@ def run_stack(args, cfg):
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(L)] for _ in range(nb)]
 
-    def step(b):
+    def step(b, timing=False):
         X.copy_(x0)
         for l, (w, lg) in enumerate(layers):
-            ML.route(lg)
+            route(lg)
             ML.permute()
-            ev[b][l][0].record()
+            if timing:
+                ev[b][l][0].record()
             ML.gateup(X, w)
-            ev[b][l][1].record()
+            if timing:
+                ev[b][l][1].record()
             ML.down(w)
             ML.combine(residual=X, out=X)
 
+    # pass 1 (value) without events between kernels; pass 2 (gate|up durations) with them
     for b in range(args.warmup):
         step(b)
     torch.cuda.synchronize()
@@ -175,6 +203,9 @@ def run_stack(args, cfg):
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
+    for b in range(args.warmup, nb):
+        step(b, timing=True)
+    torch.cuda.synchronize()
     ms_per_step = total_ms / args.steps
     value = T * args.steps / (total_ms / 1e3)
     gu_w, dn_w = expert_bytes(H, I)
@@ -184,6 +215,8 @@ def run_stack(args, cfg):
     gu_bytes = [touched[l] * gu_w + T * H * 2 + P * I * 2 for l in range(L)]
     ach = float(np.mean(gu_bytes)) / (float(np.mean(gu_us)) / 1e6) / 1e9
     step_bytes = sum(touched[l] * (gu_w + dn_w) for l in range(L)) + L * (T * E * 4 + 3 * T * H * 2)
+    if args.router:
+        step_bytes += L * (E * H * 2 + T * H * 2 + T * E * 4)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -198,7 +231,8 @@ def run_stack(args, cfg):
         "dtype": "bf16",
         "data": "synthetic (codes and scales drawn on the device)",
         "config": {"workload": cfg.name, "tokens": T, "hidden": H, "intermediate": I,
-                   "experts": E, "top_k": k, "layers": L, "residual": True},
+                   "experts": E, "top_k": k, "layers": L, "residual": True,
+                   "routing": "bf16 router, sigmoid" if args.router else "drawn logits"},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                      "traffic": profiled_traffic("decode_kernel<true>", cfg.name),
@@ -261,18 +295,23 @@ def main():
         off = L.offsets.cpu().numpy()
         touched.append(int((np.diff(off) > 0).sum()))
 
-    def step(b):
+    def step(b, ev=None):
         w = copies[b % ncopies]
         L.route(ld[b])
         L.permute()
-        ev[b][0].record()
+        if ev is not None:
+            ev[b][0].record()
         L.gateup(xd[b], w)
-        ev[b][1].record()
+        if ev is not None:
+            ev[b][1].record()
         L.down(w)
-        ev[b][2].record()
+        if ev is not None:
+            ev[b][2].record()
         L.combine()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nb)]
+    # pass 1 (value): warmup, then the timed steps with events only around the whole region (an
+    # event between two kernels leaves the GPU idle for about 5 us); pass 2: the same steps
+    # again with events around the gate|up and down launches, for their average durations
     for b in range(args.warmup):
         step(b)
     torch.cuda.synchronize()
@@ -285,6 +324,10 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     timed = range(args.warmup, nb)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nb)]
+    for b in timed:
+        step(b, ev)
+    torch.cuda.synchronize()
     gu_ms = [ev[b][0].elapsed_time(ev[b][1]) for b in timed]
     dn_ms = [ev[b][1].elapsed_time(ev[b][2]) for b in timed]
 
@@ -348,6 +391,23 @@ def main():
                   "step_TFLOP_s": round((flops_gu + flops_dn) / ms_per_step / 1e9, 2)},
         "input_setup_s": round(t_gen, 1),
     }
+
+    # the router front end (logits = X . Wr^T, bf16 in, fp32 out) on the same batches, timed on
+    # its own after the step: the workload's logits are drawn, so it is not part of the step
+    wr = torch.from_numpy(synth.make_router(cfg.cfg_id, E, H).view(np.int16)).to(dev)
+    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nb)]
+    for b in range(nb):
+        rev[b][0].record()
+        L.router(xd[b], wr)
+        rev[b][1].record()
+    torch.cuda.synchronize()
+    r_us = float(np.mean([rev[b][0].elapsed_time(rev[b][1]) for b in timed])) * 1e3
+    r_bytes = E * H * 2 + T * H * 2 + T * E * 4
+    out["router"] = {"avg_us": round(r_us, 2), "bytes_per_launch": r_bytes,
+                     "GB_s": round(r_bytes / r_us / 1e3, 1),
+                     "hbm_frac": round(r_bytes / r_us / 1e3 / HBM_PEAK_GBS, 4),
+                     "TFLOP_s": round(2.0 * T * E * H / r_us / 1e6, 2)}
 
     if args.pmc_calibrate:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)

@@ -1,11 +1,14 @@
 // Stable counting sort of the T*k (token, slot) pairs by expert, in one workgroup of 1024
-// threads (16 wavefronts), with no atomics on the order:
-//   1. expert histogram (LDS integer atomics: the counts do not depend on their order);
-//   2. wavefront prefix scan of the counts -> expert_offsets (bucket E collects invalid ids);
-//   3. pairs in chunks of 1024: the rank of a pair among the earlier same-expert pairs of its
-//      wavefront comes from ballots over the 9 bits of its bucket; a scan over the 16
-//      wavefronts per bucket gives each wavefront's starting position; positions then follow
-//      pair order within every bucket.
+// threads (16 wavefronts), with no atomics on the order. Wavefront w owns one contiguous span
+// of pairs and walks it 64 pairs at a time; within such a group, a pair's rank among the
+// earlier pairs of its bucket comes from ballots over the 9 bits of the bucket (experts
+// 0..E-1; bucket E collects ids outside [0, E)), and the group's first pair of each bucket
+// (its leader) adds the bucket's count to the wavefront's running counter.
+//   1. counting walk: per-wavefront bucket counts;
+//   2. per bucket, exclusive scans over the wavefronts and then over the buckets give every
+//      wavefront its first position in every bucket (and expert_offsets);
+//   3. placing walk: the same groups again; position = running counter + rank.
+// Positions therefore follow pair order within every bucket.
 #include "moeq_device.h"
 
 namespace moeq {
@@ -13,6 +16,7 @@ namespace moeq {
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
 constexpr int kBuckets = 257;   // experts 0..255 and one bucket for invalid ids
+constexpr int kBatch = 8;       // groups of 64 pairs per load batch
 
 // inclusive scan of one value per lane across a wavefront
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
@@ -25,21 +29,77 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v;
 }
 
+struct PairClass {
+    int bucket;
+    uint64_t same;    // lanes of this group in the same bucket (live lanes only)
+    bool live;
+};
+
+__device__ __forceinline__ PairClass classify(int e, bool live, int E) {
+    PairClass c;
+    c.live = live;
+    c.bucket = live ? ((e >= 0 && e < E) ? e : E) : 0;
+    uint64_t same = __ballot(live);
+#pragma unroll
+    for (int bit = 0; bit < 9; ++bit) {
+        const uint64_t m = __ballot((c.bucket >> bit) & 1);
+        same &= ((c.bucket >> bit) & 1) ? m : ~m;
+    }
+    c.same = same;
+    return c;
+}
+
 __global__ void __launch_bounds__(kPermThreads) permute_kernel(const int32_t* __restrict__ ids,
                                                                int P, int E,
                                                                int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ sorted_pair,
                                                                int32_t* __restrict__ pair_pos) {
-    __shared__ int cnt[kBuckets];
+    __shared__ int wcnt[kPermWaves][kBuckets];   // counts, then running positions
     __shared__ int base[kBuckets];
-    __shared__ int whist[kPermWaves][kBuckets];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t lanes_below = (1ull << lane) - 1ull;
 
-    for (int b = tid; b < kBuckets; b += kPermThreads) cnt[b] = 0;
+    for (int i = tid; i < kPermWaves * kBuckets; i += kPermThreads) (&wcnt[0][0])[i] = 0;
     __syncthreads();
-    for (int p = tid; p < P; p += kPermThreads) {
-        const int e = ids[p];
-        atomicAdd(&cnt[(e >= 0 && e < E) ? e : E], 1);
+
+    // this wavefront's span of pairs (a multiple of 64 long, except at the end of P)
+    const int span = ((P + 64 * kPermWaves - 1) / (64 * kPermWaves)) * 64;
+    const int pb = wave * span;
+    const int pe = min(P, pb + span);
+
+    // the ids of kBatch groups are loaded before the first of them is classified (one memory
+    // round trip per batch instead of one per group)
+    int idv[kBatch];
+    auto load_batch = [&](int p0) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int p = p0 + 64 * j + lane;
+            idv[j] = p < pe ? ids[p] : 0;
+        }
+    };
+
+    for (int p0 = pb; p0 < pe; p0 += 64 * kBatch) {
+        load_batch(p0);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int p = p0 + 64 * j + lane;
+            const PairClass c = classify(idv[j], p < pe, E);
+            if (c.live && __popcll(c.same & lanes_below) == 0)
+                wcnt[wave][c.bucket] += __popcll(c.same);
+        }
+    }
+    __syncthreads();
+
+    // per bucket: exclusive scan over the wavefronts (in place), total into base
+    for (int b = tid; b <= E; b += kPermThreads) {
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < kPermWaves; ++w) {
+            const int c = wcnt[w][b];
+            wcnt[w][b] = run;
+            run += c;
+        }
+        base[b] = run;
     }
     __syncthreads();
 
@@ -50,7 +110,7 @@ __global__ void __launch_bounds__(kPermThreads) permute_kernel(const int32_t* __
 #pragma unroll
         for (int j = 0; j < 5; ++j) {
             const int b = lane * 5 + j;
-            local[j] = b <= E ? cnt[b] : 0;
+            local[j] = b <= E ? base[b] : 0;
             s += local[j];
         }
         const int incl = wave_inclusive_scan(s);
@@ -67,44 +127,21 @@ __global__ void __launch_bounds__(kPermThreads) permute_kernel(const int32_t* __
     }
     __syncthreads();
 
-    const uint64_t lanes_below = (1ull << lane) - 1ull;
-    for (int p0 = 0; p0 < P; p0 += kPermThreads) {
-        for (int i = tid; i < kPermWaves * kBuckets; i += kPermThreads)
-            (&whist[0][0])[i] = 0;
-        const int p = p0 + tid;
-        const bool live = p < P;
-        int bucket = 0;
-        if (live) {
-            const int e = ids[p];
-            bucket = (e >= 0 && e < E) ? e : E;
-        }
-        uint64_t same = __ballot(live);
+    for (int p0 = pb; p0 < pe; p0 += 64 * kBatch) {
+        load_batch(p0);
 #pragma unroll
-        for (int bit = 0; bit < 9; ++bit) {
-            const uint64_t m = __ballot((bucket >> bit) & 1);
-            same &= ((bucket >> bit) & 1) ? m : ~m;
-        }
-        const int rank = __popcll(same & lanes_below);
-        __syncthreads();   // whist cleared
-        if (live && rank == 0) whist[wave][bucket] = __popcll(same);
-        __syncthreads();
-        for (int b = tid; b <= E; b += kPermThreads) {
-            int run = base[b];
-#pragma unroll
-            for (int w = 0; w < kPermWaves; ++w) {
-                const int c = whist[w][b];
-                whist[w][b] = run;
-                run += c;
+        for (int j = 0; j < kBatch; ++j) {
+            const int p = p0 + 64 * j + lane;
+            const PairClass c = classify(idv[j], p < pe, E);
+            const int rank = __popcll(c.same & lanes_below);
+            if (c.live) {
+                const int pos = base[c.bucket] + wcnt[wave][c.bucket] + rank;
+                sorted_pair[pos] = p;
+                pair_pos[p] = pos;
             }
-            base[b] = run;
+            // every lane has read its running position before the leaders advance them
+            if (c.live && rank == 0) wcnt[wave][c.bucket] += __popcll(c.same);
         }
-        __syncthreads();
-        if (live) {
-            const int pos = whist[wave][bucket] + rank;
-            sorted_pair[pos] = p;
-            pair_pos[p] = pos;
-        }
-        __syncthreads();   // before the next chunk clears whist
     }
 }
 
