@@ -21,6 +21,10 @@ Sources (the pages' titles; the section named on each function):
 * [dense6] GLM-5.2-EXL3-DENSE6-MTP78 model card, "Quant recipe": the router (mlp.gate) is held
   in BF16; [brief] "Target pipeline": a layer's routing is the router applied to its
   activations.
+* [readme] "Checkpoint layout update (2026-08-10): BF16 shared experts, merged online K6" and
+  "What changed and why": every routed layer also carries one shared-expert MLP (gate, up,
+  down projections; 5.74 GB of BF16 over the 76 layers, i.e. 3 * 6144 * 2048 weights per
+  layer) whose gate and up run as one merged launch.
 
 Readings where the pages are silent (each is listed with its reason in the design notes):
 
@@ -35,7 +39,10 @@ Readings where the pages are silent (each is listed with its reason in the desig
 * dequant rounding: the exact product, rounded once to bf16 (round-to-nearest-even);
   code 8 of a table whose entry 0 is 0 gives -0; scale byte 255 gives NaN (OCP MX E8M0);
 * the intermediate I is rounded to bf16 (the one stored activation inside the layer);
-  everything else accumulates in fp64.
+  everything else accumulates in fp64;
+* shared expert: a SwiGLU MLP of the routed experts' shape and storage format, run on every
+  token with weight 1 and added to the routed sum before the residual (the usual
+  shared-expert MoE; the pages give its tensors and size, not the sum).
 """
 from __future__ import annotations
 
@@ -44,7 +51,8 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "rne_bf16", "total_order_key", "router_logits", "route_topk",
     "permute_by_expert",
-    "unpack_codes", "dequant_bf16", "layer_forward", "stack_forward", "E2M1_TABLE",
+    "unpack_codes", "dequant_bf16", "layer_forward", "shared_expert_forward", "stack_forward",
+    "E2M1_TABLE",
 ]
 
 # [card] "What this is": the MXFP4 (E2M1) magnitudes, one per 3-bit magnitude index.
@@ -231,8 +239,29 @@ def _silu(g):
     return g / (1.0 + np.exp(-g))
 
 
+def shared_expert_forward(x_bits, sw, round_inter=True):
+    """The shared expert on every token, in fp64 ([readme] "Checkpoint layout update ...: BF16
+    shared experts, merged online K6": one gate/up/down MLP per layer beside the routed ones).
+
+    sw: weights of one expert in the routed layout (gate_codes [1, I, H/2], ..., tables,
+    table_id [1]). Per token t: I_t = bf16(silu(Wg x_t) * (Wu x_t)) (round_inter),
+    z_t = Wd I_t. Returns dict(inter=bf16 bits [T, I], z=fp64 [T, H]).
+    """
+    x = bf16_to_f64(x_bits)
+    tab = sw.tables[int(sw.table_id[0])]
+    wg = _expert_dense(sw.gate_codes[0], sw.gate_scales[0], tab)
+    wu = _expert_dense(sw.up_codes[0], sw.up_scales[0], tab)
+    a = _silu(x @ wg.T) * (x @ wu.T)
+    del wg, wu
+    inter = rne_bf16(a)
+    if round_inter:
+        a = bf16_to_f64(inter)
+    wd = _expert_dense(sw.down_codes[0], sw.down_scales[0], tab)
+    return dict(inter=inter, z=a @ wd.T)
+
+
 def layer_forward(x_bits, logits, k, lw, residual_bits=None, tokens=None, round_inter=True,
-                  routing=None):
+                  routing=None, shared=None):
     """One routed-MoE layer forward in fp64.
 
     x_bits: bf16 bits [T, H]; logits fp32 [T, E]; lw: an object with gate_codes,
@@ -246,6 +275,8 @@ def layer_forward(x_bits, logits, k, lw, residual_bits=None, tokens=None, round_
         y_t = sum_j w[t, j] * z_(t, j)  (+ residual_t)
     tokens: optional subset of token ids for which y is computed (routing is always done
     for all tokens). routing: optional precomputed (ids, w) to use instead of route_topk.
+    shared: optional shared-expert weights (see shared_expert_forward); its z_t is added to
+    y_t (for the tokens computed), and the output dict gains shared_inter and shared_z.
     Returns a dict with ids, w, offsets, sorted_pair, pair_pos, inter (bf16 bits
     [T*k, I] by sorted position; rows of tokens outside ``tokens`` are zero) and y
     (fp64 [T, H]; rows outside ``tokens`` are zero) and, with a residual, x_next bits.
@@ -291,6 +322,14 @@ def layer_forward(x_bits, logits, k, lw, residual_bits=None, tokens=None, round_
         np.add.at(y, tok, w[tok, slot][:, None] * z)
     out = dict(ids=ids, w=w, offsets=offsets, sorted_pair=sorted_pair, pair_pos=pair_pos,
                inter=inter, y=y)
+    if shared is not None:
+        rows = np.flatnonzero(want)
+        sh = shared_expert_forward(np.asarray(x_bits)[rows], shared, round_inter=round_inter)
+        y[rows] += sh["z"]
+        out["shared_inter"] = np.zeros((T, sh["inter"].shape[1]), np.uint16)
+        out["shared_inter"][rows] = sh["inter"]
+        out["shared_z"] = np.zeros((T, H), np.float64)
+        out["shared_z"][rows] = sh["z"]
     if residual_bits is not None:
         out["x_next"] = rne_bf16(bf16_to_f64(residual_bits) + y)
     return out

@@ -287,6 +287,33 @@ def make_layer(cfg_id: int, E: int, H: int, I: int, layer: int = 0, e2m1_experts
                         dict(cfg=cfg_id, layer=layer, E=E, H=H, I=I, permute=permute))
 
 
+SHARED_EXPERT_ID = 4096   # weight-stream id of a layer's shared expert (routed ids are < 256)
+
+
+def make_shared(cfg_id: int, H: int, I: int, layer: int = 0,
+                sigma: float = WEIGHT_SIGMA) -> LayerWeights:
+    """A layer's shared expert, encoded like a routed expert on the layer's own fitted grid:
+    a LayerWeights with E = 1 (table_id [0])."""
+    grid = lloyd_grid(cfg_id, layer)
+    tables = np.stack([grid, E2M1_GRID]).astype(np.float32)
+    gate_codes = np.zeros((1, I, H // 2), np.uint8)
+    up_codes = np.zeros((1, I, H // 2), np.uint8)
+    down_codes = np.zeros((1, H, I // 2), np.uint8)
+    gate_scales = np.zeros((1, I, H // 32), np.uint8)
+    up_scales = np.zeros((1, I, H // 32), np.uint8)
+    down_scales = np.zeros((1, H, I // 32), np.uint8)
+    e = SHARED_EXPERT_ID
+    rtn_normal_into(key(cfg_id, S_WEIGHTS, layer, e, 0), I, H, tables[0], gate_codes[0],
+                    gate_scales[0], sigma=sigma)
+    rtn_normal_into(key(cfg_id, S_WEIGHTS, layer, e, 1), I, H, tables[0], up_codes[0],
+                    up_scales[0], sigma=sigma)
+    rtn_normal_into(key(cfg_id, S_WEIGHTS, layer, e, 2), H, I, tables[0], down_codes[0],
+                    down_scales[0], sigma=sigma)
+    return LayerWeights(gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales,
+                        tables, np.zeros(1, np.uint8), None,
+                        dict(cfg=cfg_id, layer=layer, E=1, H=H, I=I, permute=None, shared=True))
+
+
 # ----------------------------------------------------------------------------------------------
 # the five workloads
 # ----------------------------------------------------------------------------------------------

@@ -416,3 +416,68 @@ def test_stack_residual_rounding(tiny):
     two = oracle.stack_forward(x, [(logits, lw), (logits, lw)], c.k)
     step = oracle.layer_forward(one["x_next"], logits, c.k, lw, residual_bits=one["x_next"])
     np.testing.assert_array_equal(two, step["x_next"])
+
+
+# ----------------------------------------------------------------------------------------------
+# shared expert
+# ----------------------------------------------------------------------------------------------
+
+def _with_shared_as_expert(lw, sw):
+    """The routed layer with the shared expert appended as expert E (same table set)."""
+    assert np.array_equal(lw.tables, sw.tables)
+    cat = lambda a, b: np.concatenate([a, b], axis=0)
+    return synth.LayerWeights(cat(lw.gate_codes, sw.gate_codes), cat(lw.gate_scales, sw.gate_scales),
+                              cat(lw.up_codes, sw.up_codes), cat(lw.up_scales, sw.up_scales),
+                              cat(lw.down_codes, sw.down_codes), cat(lw.down_scales, sw.down_scales),
+                              lw.tables, cat(lw.table_id, sw.table_id))
+
+
+def test_shared_expert_is_a_routed_expert_with_weight_one(tiny):
+    """Adding the shared expert equals routing every token to one more expert, the shared one,
+    with gate weight 1 (through the routed path pinned above)."""
+    c, lw, x, logits = tiny
+    sw = synth.make_shared(1, c.H, c.I)
+    out = oracle.layer_forward(x, logits, c.k, lw, shared=sw, residual_bits=x)
+    ids = np.concatenate([out["ids"], np.full((c.T, 1), c.E, np.int32)], axis=1)
+    w = np.concatenate([out["w"], np.ones((c.T, 1))], axis=1)
+    aug = oracle.layer_forward(x, None, c.k + 1, _with_shared_as_expert(lw, sw), routing=(ids, w),
+                               residual_bits=x)
+    np.testing.assert_allclose(out["y"], aug["y"], rtol=1e-12, atol=1e-14)
+    shared_rows = aug["pair_pos"].reshape(c.T, c.k + 1)[:, c.k]
+    np.testing.assert_array_equal(out["shared_inter"], aug["inter"][shared_rows])
+    assert not np.array_equal(out["y"], oracle.layer_forward(x, logits, c.k, lw)["y"])
+
+
+def test_shared_expert_matches_glm4_moe_mlp(tiny):
+    """Against transformers' GLM-4.5 MoE dense MLP (its shared-expert module) on the dequantized
+    weights, in fp64 without the bf16 rounding of the intermediate."""
+    import torch
+    from transformers import Glm4MoeConfig
+    from transformers.models.glm4_moe.modeling_glm4_moe import Glm4MoeMLP
+    c, _, x, _ = tiny
+    sw = synth.make_shared(1, c.H, c.I)
+    g, u, d = _dense(sw)
+    cfg = Glm4MoeConfig(hidden_size=c.H, intermediate_size=c.I, hidden_act="silu")
+    mlp = Glm4MoeMLP(cfg, intermediate_size=c.I).double()
+    with torch.no_grad():
+        mlp.gate_proj.weight.copy_(torch.from_numpy(g[0]))
+        mlp.up_proj.weight.copy_(torch.from_numpy(u[0]))
+        mlp.down_proj.weight.copy_(torch.from_numpy(d[0]))
+        ref = mlp(torch.from_numpy(oracle.bf16_to_f64(x))).numpy()
+    z = oracle.shared_expert_forward(x, sw, round_inter=False)["z"]
+    np.testing.assert_allclose(z, ref, rtol=1e-12, atol=1e-14)
+    # with the intermediate rounded, the stored inter is bf16 of SwiGLU
+    sh = oracle.shared_expert_forward(x, sw)
+    a = oracle.bf16_to_f64(x) @ g[0].T
+    np.testing.assert_array_equal(sh["inter"], oracle.rne_bf16(a / (1 + np.exp(-a)) *
+                                                             (oracle.bf16_to_f64(x) @ u[0].T)))
+
+
+def test_shared_expert_token_subset(tiny):
+    c, lw, x, logits = tiny
+    sw = synth.make_shared(1, c.H, c.I)
+    full = oracle.layer_forward(x, logits, c.k, lw, shared=sw)
+    part = oracle.layer_forward(x, logits, c.k, lw, shared=sw, tokens=[3, 11])
+    np.testing.assert_array_equal(part["y"][[3, 11]], full["y"][[3, 11]])
+    np.testing.assert_array_equal(part["shared_z"][[3, 11]], full["shared_z"][[3, 11]])
+    assert not part["y"][0].any()
