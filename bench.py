@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2,
                     help="tokens of the workload the CPU oracle is timed on")
+    ap.add_argument("--shared", action="store_true",
+                    help="layer workloads: add a shared expert (the routed experts' shape and "
+                         "format, every token, weight 1) on a side stream, summed in the combine")
     ap.add_argument("--router", action="store_true",
                     help="stack: route every layer from its activations through a bf16 router "
                          "(logits = X . Wr^T, sigmoid gating) instead of pre-drawn logits")
@@ -283,7 +286,10 @@ def main():
         lgs.append(synth.make_logits(cfg.cfg_id, T, E, zipf_s=cfg.zipf_s, batch=b))
     xd = [torch.from_numpy(x.view(np.int16)).to(dev) for x in xs]
     ld = [torch.from_numpy(l).to(dev) for l in lgs]
-    L = mq.MoeLayer(T, H, I, E, k)
+    sw = None
+    if args.shared:
+        sw = mq.DeviceWeights.from_host(synth.make_shared(cfg.cfg_id, H, I))
+    L = mq.MoeLayer(T, H, I, E, k, shared_I=I if sw is not None else None)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
 
@@ -297,6 +303,17 @@ def main():
 
     def step(b, ev=None):
         w = copies[b % ncopies]
+        if sw is not None:
+            # the shared expert on the side stream, beside the routed path
+            main = torch.cuda.current_stream()
+            L.fork.record(main)
+            L.side.wait_event(L.fork)
+            if ev is not None:
+                ev[b][3].record(L.side)
+            L.shared_expert(xd[b], sw, stream=L.side)
+            if ev is not None:
+                ev[b][4].record(L.side)
+            L.join.record(L.side)
         L.route(ld[b])
         L.permute()
         if ev is not None:
@@ -307,7 +324,9 @@ def main():
         L.down(w)
         if ev is not None:
             ev[b][2].record()
-        L.combine()
+        if sw is not None:
+            main.wait_event(L.join)
+        L.combine(shared=sw is not None)
 
     # pass 1 (value): warmup, then the timed steps with events only around the whole region (an
     # event between two kernels leaves the GPU idle for about 5 us); pass 2: the same steps
@@ -324,18 +343,23 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     timed = range(args.warmup, nb)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nb)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nb)]
     for b in timed:
         step(b, ev)
     torch.cuda.synchronize()
     gu_ms = [ev[b][0].elapsed_time(ev[b][1]) for b in timed]
     dn_ms = [ev[b][1].elapsed_time(ev[b][2]) for b in timed]
+    sh_ms = [ev[b][3].elapsed_time(ev[b][4]) for b in timed] if sw is not None else None
 
     gu_w, dn_w = expert_bytes(H, I)
     P = T * k
     gu_bytes = [touched[b] * gu_w + T * H * 2 + P * I * 2 for b in timed]
     dn_bytes = [touched[b] * dn_w + P * I * 2 + P * H * 4 + P * 4 for b in timed]
     step_bytes = [touched[b] * (gu_w + dn_w) + T * E * 4 + 2 * T * H * 2 for b in timed]
+    if sw is not None:
+        # the shared expert's weights, its intermediate out and in, z out and in
+        sh_bytes = gu_w + dn_w + T * H * 2 + 2 * T * I * 2 + 2 * T * H * 4
+        step_bytes = [sb + sh_bytes for sb in step_bytes]
     flops_gu = 2.0 * P * 2 * I * H
     flops_dn = 2.0 * P * H * I
 
@@ -371,7 +395,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": T, "hidden": H, "intermediate": I,
                    "experts": E, "top_k": k, "zipf_s": cfg.zipf_s,
                    "e2m1_experts": list(cfg.e2m1), "channel_permutation": cfg.permute,
-                   "weight_copies": ncopies},
+                   "weight_copies": ncopies, "shared_expert": sw is not None},
         "roofline": roof,
         "kernels": {
             "gateup_swiglu": {"avg_us": round(gu_avg * 1e3, 2),
@@ -388,9 +412,18 @@ def main():
                   "step_GB_s": round(float(np.mean(step_bytes)) / ms_per_step / 1e6, 1),
                   "step_hbm_frac": round(float(np.mean(step_bytes)) / ms_per_step / 1e6
                                          / HBM_PEAK_GBS, 4),
-                  "step_TFLOP_s": round((flops_gu + flops_dn) / ms_per_step / 1e9, 2)},
+                  "step_TFLOP_s": round((flops_gu + flops_dn + (2.0 * T * 3 * H * I if sw
+                                                                  is not None else 0.0))
+                                        / ms_per_step / 1e9, 2)},
         "input_setup_s": round(t_gen, 1),
     }
+
+    if sw is not None:
+        sh_us = float(np.mean(sh_ms)) * 1e3
+        out["shared_expert"] = {"avg_us_on_side_stream": round(sh_us, 2),
+                                "bytes_per_call": int(sh_bytes),
+                                "GB_s": round(sh_bytes / sh_us / 1e3, 1),
+                                "TFLOP_s": round(2.0 * T * 3 * H * I / sh_us / 1e6, 2)}
 
     # the router front end (logits = X . Wr^T, bf16 in, fp32 out) on the same batches, timed on
     # its own after the step: the workload's logits are drawn, so it is not part of the step

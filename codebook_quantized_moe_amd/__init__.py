@@ -32,7 +32,8 @@ MAX_TABLES = 4
 
 EXPORTED = ("moeq_last_error", "moeq_workspace_bytes", "moeq_router_logits", "moeq_route_topk",
             "moeq_permute_by_expert", "moeq_gateup_swiglu", "moeq_down",
-            "moeq_unpermute_combine", "moeq_debug_dequant")
+            "moeq_unpermute_combine", "moeq_shared_workspace_bytes", "moeq_shared_expert",
+            "moeq_unpermute_combine_shared", "moeq_debug_dequant")
 
 _i, _vp, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
 _lib.moeq_last_error.restype = ctypes.c_char_p
@@ -53,6 +54,13 @@ _lib.moeq_down.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp
                            _vp, _sz, _vp]
 _lib.moeq_unpermute_combine.restype = _i
 _lib.moeq_unpermute_combine.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
+_lib.moeq_shared_workspace_bytes.restype = _sz
+_lib.moeq_shared_workspace_bytes.argtypes = [_i] * 3
+_lib.moeq_shared_expert.restype = _i
+_lib.moeq_shared_expert.argtypes = [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp,
+                                    _vp, _vp, _vp, _sz, _vp]
+_lib.moeq_unpermute_combine_shared.restype = _i
+_lib.moeq_unpermute_combine_shared.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]
 _lib.moeq_debug_dequant.restype = _i
 _lib.moeq_debug_dequant.argtypes = [_vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _vp]
 
@@ -140,6 +148,26 @@ def moeq_down(inter, T, H, I, E, k, expert_offsets, sorted_pair, topk_w, down_co
 def moeq_unpermute_combine(yp, pair_pos, expert_offsets, T, k, E, H, residual, y, stream=None):
     _check(_lib.moeq_unpermute_combine(_p(yp), _p(pair_pos), _p(expert_offsets), T, k, E, H,
                                        _p(residual), _p(y), _stream(stream)))
+
+
+def moeq_shared_workspace_bytes(T: int, H: int, I: int) -> int:
+    return int(_lib.moeq_shared_workspace_bytes(T, H, I))
+
+
+def moeq_shared_expert(x, T, H, I, gate_codes, gate_scales, up_codes, up_scales, down_codes,
+                       down_scales, tables, table_id, inter, z, ws, ws_bytes, stream=None):
+    tab, n = _tables(tables)
+    _check(_lib.moeq_shared_expert(_p(x), T, H, I, _p(gate_codes), _p(gate_scales), _p(up_codes),
+                                   _p(up_scales), _p(down_codes), _p(down_scales), tab.ctypes.data,
+                                   n, _p(table_id), _p(inter), _p(z), _p(ws), ws_bytes,
+                                   _stream(stream)))
+
+
+def moeq_unpermute_combine_shared(yp, pair_pos, expert_offsets, T, k, E, H, shared_z, residual,
+                                  y, stream=None):
+    _check(_lib.moeq_unpermute_combine_shared(_p(yp), _p(pair_pos), _p(expert_offsets), T, k, E,
+                                              H, _p(shared_z), _p(residual), _p(y),
+                                              _stream(stream)))
 
 
 def moeq_debug_dequant(codes, scales, E, N, K, tables, table_id, out, stream=None):

@@ -176,7 +176,7 @@ static int projection(const char* w, bool gateup, const uint16_t* act, int T, in
                       const uint8_t* codes0, const uint8_t* scales0, const uint8_t* codes1,
                       const uint8_t* scales1, const float* tables, int n_tables,
                       const uint8_t* table_id, void* out, void* ws, size_t ws_bytes,
-                      hipStream_t stream) {
+                      hipStream_t stream, bool launch = true) {
     if (int r = check_sizes(w, T, k, E)) return r;
     if (int r = check_hk(w, H, I)) return r;
     SkinnyArgs a;
@@ -197,7 +197,7 @@ static int projection(const char* w, bool gateup, const uint16_t* act, int T, in
     const long long mat_bytes = gateup ? (long long)I * H / 2 : (long long)H * I / 2;
     if (act_bytes >= (1LL << 31) || mat_bytes >= (1LL << 31))
         return fail(MOEQ_EUNSUPPORTED, "%s: activations and each expert matrix must stay below 2 GiB", w);
-    if (T == 0) return ok();
+    if (T == 0 || !launch) return ok();
     a.act = act;
     a.act_bytes = (uint32_t)act_bytes;
     a.offsets = offsets;
@@ -260,19 +260,83 @@ int moeq_down(const uint16_t* inter, int T, int H, int I, int E, int k,
                       ws_bytes, (hipStream_t)stream);
 }
 
-int moeq_unpermute_combine(const float* yp, const int32_t* pair_pos, const int32_t* expert_offsets,
-                           int T, int k, int E, int H, const uint16_t* residual, uint16_t* y,
-                           void* stream) {
-    const char* w = "moeq_unpermute_combine";
+static int combine(const char* w, const float* yp, const int32_t* pair_pos,
+                   const int32_t* expert_offsets, int T, int k, int E, int H,
+                   const float* shared_z, const uint16_t* residual, uint16_t* y,
+                   hipStream_t stream) {
     if (int r = check_sizes(w, T, k, E)) return r;
     if (H <= 0 || H % 4) return fail(MOEQ_EUNSUPPORTED, "%s: H = %d must be a positive multiple of 4", w, H);
     if (T == 0) return ok();
     if (!yp || !pair_pos || !expert_offsets || !y) return fail(MOEQ_EINVAL, "%s: null pointer", w);
-    if (!aligned(yp, 16) || !aligned(y, 8) || (residual && !aligned(residual, 8)))
-        return fail(MOEQ_EUNSUPPORTED, "%s: yp must be 16-byte aligned, y and residual 8-byte aligned", w);
+    if (!aligned(yp, 16) || !aligned(y, 8) || (residual && !aligned(residual, 8)) ||
+        (shared_z && !aligned(shared_z, 16)))
+        return fail(MOEQ_EUNSUPPORTED, "%s: yp and shared_z must be 16-byte aligned, y and residual 8-byte aligned", w);
     clear_hip_error();
-    launch_combine(yp, pair_pos, expert_offsets, T, k, E, H, residual, y, (hipStream_t)stream);
+    launch_combine(yp, pair_pos, expert_offsets, T, k, E, H, shared_z, residual, y, stream);
     return check_launch(w);
+}
+
+int moeq_unpermute_combine(const float* yp, const int32_t* pair_pos, const int32_t* expert_offsets,
+                           int T, int k, int E, int H, const uint16_t* residual, uint16_t* y,
+                           void* stream) {
+    return combine("moeq_unpermute_combine", yp, pair_pos, expert_offsets, T, k, E, H, nullptr,
+                   residual, y, (hipStream_t)stream);
+}
+
+int moeq_unpermute_combine_shared(const float* yp, const int32_t* pair_pos,
+                                  const int32_t* expert_offsets, int T, int k, int E, int H,
+                                  const float* shared_z, const uint16_t* residual, uint16_t* y,
+                                  void* stream) {
+    return combine("moeq_unpermute_combine_shared", yp, pair_pos, expert_offsets, T, k, E, H,
+                   shared_z, residual, y, (hipStream_t)stream);
+}
+
+size_t moeq_shared_workspace_bytes(int T, int H, int I) {
+    if (T <= 0 || H <= 0) return 0;
+    return shared_routing_bytes(T) + moeq_workspace_bytes(T, 1, 1, H, I);
+}
+
+int moeq_shared_expert(const uint16_t* x, int T, int H, int I, const uint8_t* gate_codes,
+                       const uint8_t* gate_scales, const uint8_t* up_codes,
+                       const uint8_t* up_scales, const uint8_t* down_codes,
+                       const uint8_t* down_scales, const float* tables, int n_tables,
+                       const uint8_t* table_id, uint16_t* inter, float* z, void* ws,
+                       size_t ws_bytes, void* stream) {
+    const char* w = "moeq_shared_expert";
+    if (T < 0 || H <= 0) return fail(MOEQ_EINVAL, "%s: bad sizes T=%d H=%d", w, T, H);
+    if (T == 0) return ok();
+    const size_t need = moeq_shared_workspace_bytes(T, H, I);
+    if (!ws || ws_bytes < need)
+        return fail(MOEQ_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", w, need, ws_bytes);
+    if (!aligned(ws, 256))
+        return fail(MOEQ_EUNSUPPORTED, "%s: the workspace must be 256-byte aligned", w);
+    // workspace: identity routing (offsets {0, T}, sorted_pair = 0..T-1, gate weights 1), then
+    // the projections' own workspace
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    int32_t* offsets = reinterpret_cast<int32_t*>(base);
+    int32_t* sorted_pair = reinterpret_cast<int32_t*>(base + 256);
+    float* ones = reinterpret_cast<float*>(base + 256 + shared_rows_bytes(T));
+    void* pws = base + shared_routing_bytes(T);
+    const size_t pws_bytes = need - shared_routing_bytes(T);
+    // validate both projections before launching anything
+    if (int r = projection(w, true, x, T, H, I, 1, 1, offsets, sorted_pair, nullptr, gate_codes,
+                           gate_scales, up_codes, up_scales, tables, n_tables, table_id, inter,
+                           pws, pws_bytes, (hipStream_t)stream, false))
+        return r;
+    if (int r = projection(w, false, inter, T, H, I, 1, 1, offsets, sorted_pair, ones, down_codes,
+                           down_scales, nullptr, nullptr, tables, n_tables, table_id, z, pws,
+                           pws_bytes, (hipStream_t)stream, false))
+        return r;
+    clear_hip_error();
+    launch_identity_routing(T, offsets, sorted_pair, ones, (hipStream_t)stream);
+    if (int r = check_launch(w)) return r;
+    if (int r = projection(w, true, x, T, H, I, 1, 1, offsets, sorted_pair, nullptr, gate_codes,
+                           gate_scales, up_codes, up_scales, tables, n_tables, table_id, inter,
+                           pws, pws_bytes, (hipStream_t)stream))
+        return r;
+    return projection(w, false, inter, T, H, I, 1, 1, offsets, sorted_pair, ones, down_codes,
+                      down_scales, nullptr, nullptr, tables, n_tables, table_id, z, pws, pws_bytes,
+                      (hipStream_t)stream);
 }
 
 int moeq_debug_dequant(const uint8_t* codes, const uint8_t* scales, int E, int N, int K,

@@ -46,7 +46,13 @@ size_t prefill_queue_bytes();
 void launch_pair_split_rows(const uint16_t* x, int T, int H, uint16_t* xs, int cus,
                             hipStream_t stream);
 void launch_combine(const float* yp, const int32_t* pair_pos, const int32_t* offsets, int T, int k,
-                    int E, int H, const uint16_t* residual, uint16_t* y, hipStream_t stream);
+                    int E, int H, const float* shared_z, const uint16_t* residual, uint16_t* y,
+                    hipStream_t stream);
+// shared expert: routing of every token to one expert with weight 1, in the workspace
+inline size_t shared_rows_bytes(int T) { return ((size_t)T * 4 + 255) / 256 * 256; }
+inline size_t shared_routing_bytes(int T) { return 256 + 2 * shared_rows_bytes(T); }
+void launch_identity_routing(int T, int32_t* offsets, int32_t* sorted_pair, float* w,
+                             hipStream_t stream);
 void launch_dequant(const uint8_t* codes, const uint8_t* scales, int E, int N, int K,
                     const uint8_t* table_id, const TableArgs& ta, uint16_t* out, int blocks,
                     hipStream_t stream);

@@ -12,7 +12,9 @@ import numpy as np
 import torch
 
 from . import (MOEQ_GATING_SOFTMAX_TOPK, moeq_down, moeq_gateup_swiglu, moeq_permute_by_expert,
-               moeq_route_topk, moeq_router_logits, moeq_unpermute_combine, moeq_workspace_bytes)
+               moeq_route_topk, moeq_router_logits, moeq_shared_expert,
+               moeq_shared_workspace_bytes, moeq_unpermute_combine,
+               moeq_unpermute_combine_shared, moeq_workspace_bytes)
 
 
 @dataclass
@@ -49,12 +51,22 @@ class DeviceWeights:
 
 
 class MoeLayer:
-    """Preallocated buffers for T tokens of a layer with E experts, top-k."""
+    """Preallocated buffers for T tokens of a layer with E experts, top-k (and, with
+    shared_I, a shared expert of intermediate size shared_I)."""
 
     def __init__(self, T: int, H: int, I: int, E: int, k: int, device="cuda",
-                 gating: int = MOEQ_GATING_SOFTMAX_TOPK):
+                 gating: int = MOEQ_GATING_SOFTMAX_TOPK, shared_I: int | None = None):
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
         self.gating = gating
+        self.shared_I = shared_I
+        if shared_I is not None:
+            self.s_inter = torch.empty((T, shared_I), dtype=torch.int16, device=device)
+            self.s_z = torch.empty((T, H), dtype=torch.float32, device=device)
+            self.s_ws_bytes = moeq_shared_workspace_bytes(T, H, shared_I)
+            self.s_ws = torch.empty(max(self.s_ws_bytes, 1), dtype=torch.uint8, device=device)
+            self.side = torch.cuda.Stream(device=device)      # default priority
+            self.fork = torch.cuda.Event()
+            self.join = torch.cuda.Event()
         P = T * k
         i32 = dict(dtype=torch.int32, device=device)
         self.logits = torch.empty((T, E), dtype=torch.float32, device=device)
@@ -93,26 +105,57 @@ class MoeLayer:
                   self.sorted_pair, self.topk_w, w.down_codes, w.down_scales, w.tables,
                   w.table_id, self.yp, self.ws, self.ws_bytes, stream=stream)
 
-    def combine(self, residual=None, out=None, stream=None):
+    def shared_expert(self, x, sw: DeviceWeights, stream=None):
+        """The shared expert (E = 1 weights) on every token into self.s_z."""
+        moeq_shared_expert(x, self.T, self.H, self.shared_I, sw.gate_codes, sw.gate_scales,
+                           sw.up_codes, sw.up_scales, sw.down_codes, sw.down_scales, sw.tables,
+                           sw.table_id, self.s_inter, self.s_z, self.s_ws, self.s_ws_bytes,
+                           stream=stream)
+
+    def combine(self, residual=None, out=None, stream=None, shared=False):
         out = self.y if out is None else out
-        moeq_unpermute_combine(self.yp, self.pair_pos, self.offsets, self.T, self.k, self.E,
-                               self.H, residual, out, stream=stream)
+        if shared:
+            moeq_unpermute_combine_shared(self.yp, self.pair_pos, self.offsets, self.T, self.k,
+                                          self.E, self.H, self.s_z, residual, out, stream=stream)
+        else:
+            moeq_unpermute_combine(self.yp, self.pair_pos, self.offsets, self.T, self.k, self.E,
+                                   self.H, residual, out, stream=stream)
         return out
 
-    def forward(self, x, logits, w: DeviceWeights, residual=None, out=None, stream=None):
-        """x: int16 (bf16 bits) [T, H] cuda; logits fp32 [T, E] cuda. Returns y (bf16 bits)."""
+    def _fork_shared(self, x, sw, stream):
+        """Start the shared expert on the side stream once x is ready on the main stream."""
+        main = stream if stream is not None else torch.cuda.current_stream()
+        self.fork.record(main)
+        self.side.wait_event(self.fork)
+        self.shared_expert(x, sw, stream=self.side)
+        self.join.record(self.side)
+        return main
+
+    def forward(self, x, logits, w: DeviceWeights, residual=None, out=None, stream=None,
+                shared: DeviceWeights | None = None):
+        """x: int16 (bf16 bits) [T, H] cuda; logits fp32 [T, E] cuda. Returns y (bf16 bits).
+        With shared weights, the shared expert runs on a side stream beside the routed path
+        and is added in the combine."""
+        if shared is not None:
+            stream = self._fork_shared(x, shared, stream)
         self.route(logits, stream)
         self.permute(stream)
         self.gateup(x, w, stream)
         self.down(w, stream)
-        return self.combine(residual, out, stream)
+        if shared is not None:
+            stream.wait_event(self.join)
+        return self.combine(residual, out, stream, shared=shared is not None)
 
     def forward_routed(self, x, router_w, w: DeviceWeights, residual=None, out=None,
-                       stream=None):
+                       stream=None, shared: DeviceWeights | None = None):
         """As forward, with the logits computed from x by the bf16 router router_w [E, H]."""
+        if shared is not None:
+            stream = self._fork_shared(x, shared, stream)
         self.router(x, router_w, stream)
         self.route(self.logits, stream)
         self.permute(stream)
         self.gateup(x, w, stream)
         self.down(w, stream)
-        return self.combine(residual, out, stream)
+        if shared is not None:
+            stream.wait_event(self.join)
+        return self.combine(residual, out, stream, shared=shared is not None)

@@ -197,6 +197,51 @@ int moeq_unpermute_combine(const float* yp, const int32_t* pair_pos, const int32
                            void* stream);
 
 /*
+ * The shared expert (README of GLM-5.2-EXL3-TR3v4-3.5bpw-MTP78, "Checkpoint layout update
+ * (2026-08-10): BF16 shared experts, merged online K6" and "What changed and why": each routed
+ * layer also carries one shared gate/up/down MLP, 3 x 6144 x 2048 weights, with gate and up
+ * merged into one launch). Stored here in the routed experts' 4-bit format and run on every
+ * token with weight 1 by the same projection kernels, gate|up merged:
+ *     inter[t][moeq_inter_slot(n)] = bf16(silu(X[t] . Wg[n]) * (X[t] . Wu[n]))
+ *     z[t] = inter[t] . Wd^T                           (fp32)
+ *   x        bf16 [T, H]
+ *   gate/up codes uint8 [I, H/2], scales uint8 [I, H/32]; down codes uint8 [H, I/2], scales
+ *            uint8 [H, I/32] (one expert of the routed layout)
+ *   tables   HOST fp32 [n_tables][8] as for the routed projections; table_id uint8 [1] on the
+ *            device (an id >= n_tables writes NaN rows)
+ *   inter    bf16 [T, I] out (row t = token t)
+ *   z        fp32 [T, H] out, for moeq_unpermute_combine_shared
+ *   ws       moeq_shared_workspace_bytes(T, H, I) bytes, 256-byte aligned: the identity
+ *            routing of the call (offsets, rows, unit gate weights) and the projections'
+ *            workspace. Scratch between calls; calls that run at the same time (the shared
+ *            expert on its own stream beside the routed path, say) need their own.
+ * Sizes and alignment as for moeq_gateup_swiglu / moeq_down with E = 1, k = 1. T = 0 is a
+ * no-op. Errors: MOEQ_EINVAL for null pointers or bad sizes, MOEQ_EUNSUPPORTED for shapes or
+ * alignment, MOEQ_EWORKSPACE for a missing or short workspace; both projections are validated
+ * before anything is launched.
+ */
+size_t moeq_shared_workspace_bytes(int T, int H, int I);
+int moeq_shared_expert(const uint16_t* x, int T, int H, int I, const uint8_t* gate_codes,
+                       const uint8_t* gate_scales, const uint8_t* up_codes,
+                       const uint8_t* up_scales, const uint8_t* down_codes,
+                       const uint8_t* down_scales, const float* tables, int n_tables,
+                       const uint8_t* table_id, uint16_t* inter, float* z, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * moeq_unpermute_combine with the shared expert's output added after the routed slots and
+ * before the residual, all in fp32 (the same README, "Checkpoint layout update"):
+ *     y[t] = bf16( sum_j yp[pair_pos[t*k + j]] + shared_z[t]  (+ residual[t]) )
+ *   shared_z fp32 [T, H] from moeq_shared_expert, 16-byte aligned, or NULL (then the call is
+ *            moeq_unpermute_combine)
+ * Other arguments and errors as for moeq_unpermute_combine.
+ */
+int moeq_unpermute_combine_shared(const float* yp, const int32_t* pair_pos,
+                                  const int32_t* expert_offsets, int T, int k, int E, int H,
+                                  const float* shared_z, const uint16_t* residual, uint16_t* y,
+                                  void* stream);
+
+/*
  * Test entry point: decode whole matrices with the same device decode path the two
  * projections use (model card, "Codes are indices into the per-layer grid").
  *   codes uint8 [E, N, K/2], scales uint8 [E, N, K/32], out bf16 [E, N, K] (natural K order)

@@ -156,3 +156,48 @@ def test_workspace_contract():
     assert _status(mq.moeq_gateup_swiglu, **_gateup(ws=FAKE + 8, ws_bytes=need)) == \
         mq.MOEQ_EUNSUPPORTED
     assert str(need) in mq.moeq_last_error() or "aligned" in mq.moeq_last_error()
+
+
+def _shared(**over):
+    ws_need = mq.moeq_shared_workspace_bytes(8, 6144, 2048)
+    a = dict(x=FAKE, T=8, H=6144, I=2048, gate_codes=FAKE, gate_scales=FAKE, up_codes=FAKE,
+             up_scales=FAKE, down_codes=FAKE, down_scales=FAKE, tables=GOOD_TABLES,
+             table_id=FAKE, inter=FAKE, z=FAKE, ws=FAKE, ws_bytes=ws_need, stream=0)
+    a.update(over)
+    return a
+
+
+def test_shared_expert_contract():
+    # identity routing (256 + 2 * 256-rounded T ints) + the projections' workspace for T rows
+    assert mq.moeq_shared_workspace_bytes(8, 6144, 2048) == \
+        256 + 2 * 256 + mq.moeq_workspace_bytes(8, 1, 1, 6144, 2048)
+    assert mq.moeq_shared_workspace_bytes(100, 64, 64) == \
+        256 + 2 * 512 + mq.moeq_workspace_bytes(100, 1, 1, 64, 64)
+    assert mq.moeq_shared_workspace_bytes(0, 6144, 2048) == 0
+    need = mq.moeq_shared_workspace_bytes(8, 6144, 2048)
+    bad = [
+        (dict(ws=None), mq.MOEQ_EWORKSPACE),
+        (dict(ws_bytes=need - 1), mq.MOEQ_EWORKSPACE),
+        (dict(ws=FAKE + 16), mq.MOEQ_EUNSUPPORTED),         # 256-byte alignment
+        (dict(H=6000, ws_bytes=1 << 30), mq.MOEQ_EUNSUPPORTED),
+        (dict(I=100), mq.MOEQ_EUNSUPPORTED),
+        (dict(T=-1), mq.MOEQ_EINVAL),
+        (dict(x=None), mq.MOEQ_EINVAL),
+        (dict(down_codes=None), mq.MOEQ_EINVAL),           # the down projection is checked too
+        (dict(down_scales=FAKE + 2), mq.MOEQ_EUNSUPPORTED),
+        (dict(z=FAKE + 4), mq.MOEQ_EUNSUPPORTED),
+        (dict(table_id=None), mq.MOEQ_EINVAL),
+        (dict(tables=np.array([[np.nan] * 8], np.float32)), mq.MOEQ_EINVAL),
+    ]
+    for over, code in bad:
+        assert _status(mq.moeq_shared_expert, **_shared(**over)) == code, over
+        assert "moeq_shared_expert" in mq.moeq_last_error()
+    mq.moeq_shared_expert(**_shared(T=0, x=None, ws=None, ws_bytes=0))   # T = 0: no-op, OK
+    f = mq.moeq_unpermute_combine_shared
+    assert _status(f, FAKE, FAKE, FAKE, 8, 8, 256, 6144, FAKE + 4, None, FAKE,
+                   stream=0) == mq.MOEQ_EUNSUPPORTED
+    assert _status(f, FAKE, FAKE, FAKE, 8, 8, 256, 6146, FAKE, None, FAKE,
+                   stream=0) == mq.MOEQ_EUNSUPPORTED
+    assert _status(f, None, FAKE, FAKE, 8, 8, 256, 6144, FAKE, None, FAKE,
+                   stream=0) == mq.MOEQ_EINVAL
+    f(None, None, None, 0, 8, 256, 6144, None, None, None, stream=0)   # T = 0: no-op, OK

@@ -470,3 +470,82 @@ def test_block_permutation_relayout_gpu(path):
     rel = np.linalg.norm(a - b, axis=1) / np.linalg.norm(a, axis=1)
     assert rel.max() < 1e-3
     assert np.median(rel) < 1e-6
+
+
+# ----------------------------------------------------------------------------------------------
+# shared expert beside the routed ones
+# ----------------------------------------------------------------------------------------------
+
+def _run_shared(sw, x):
+    mq = _mq()
+    T, H = x.shape
+    I = sw.gate_codes.shape[1]
+    w = mq.DeviceWeights.from_host(sw)
+    inter = torch.empty((T, I), dtype=torch.int16, device="cuda")
+    z = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    nws = mq.moeq_shared_workspace_bytes(T, H, I)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    mq.moeq_shared_expert(dev(x.view(np.int16)), T, H, I, w.gate_codes, w.gate_scales,
+                          w.up_codes, w.up_scales, w.down_codes, w.down_scales, w.tables,
+                          w.table_id, inter, z, ws, nws)
+    return u16(inter), host(z)
+
+
+@pytest.mark.parametrize("T,H,I", [(16, 256, 128),       # tiny geometry
+                                   (37, 576, 320),       # K tails, ragged rows
+                                   (1, 256, 128),        # one token
+                                   (8, 6144, 2048),      # GLM decode batch
+                                   (200, 1024, 512)])    # many rows (prefill kernels)
+def test_shared_expert(T, H, I, path):
+    sw = synth.make_shared(41, H, I)
+    x = synth.make_x(41, T, H)
+    inter, z = _run_shared(sw, x)
+    ref = oracle.shared_expert_forward(x, sw)
+    gi = oracle.bf16_to_f64(unslot(inter, I))
+    ri = oracle.bf16_to_f64(ref["inter"])
+    rel_i = np.linalg.norm(gi - ri, axis=1) / np.linalg.norm(ri, axis=1)
+    assert rel_i.max() < ROW_REL_TOL, rel_i.max()
+    rel = np.linalg.norm(z - ref["z"], axis=1) / np.linalg.norm(ref["z"], axis=1)
+    assert np.all(np.isfinite(z)) and rel.max() <= ROW_REL_TOL, rel.max()
+
+
+def test_shared_expert_invalid_table_id_gives_nan():
+    sw = synth.make_shared(42, 256, 128)
+    sw.table_id[0] = 5
+    _, z = _run_shared(sw, synth.make_x(42, 4, 256))
+    assert np.isnan(z).all()
+
+
+@pytest.mark.parametrize("T,E,H,I,k", [(16, 4, 256, 128, 2), (37, 8, 576, 320, 4)])
+def test_layer_with_shared_expert(T, E, H, I, k, path):
+    """Routed path on the main stream, the shared expert on a side stream, summed in the
+    combine with the residual; y in place over X."""
+    mq = _mq()
+    lw, x, logits = _case(43, T, E, H, I, k, e2m1_experts=(1,), permute="random")
+    sw = synth.make_shared(43, H, I)
+    L = mq.MoeLayer(T, H, I, E, k, shared_I=I)
+    xb = dev(x.view(np.int16))
+    L.forward(xb, dev(logits), mq.DeviceWeights.from_host(lw), residual=xb, out=xb,
+              shared=mq.DeviceWeights.from_host(sw))
+    ref = oracle.layer_forward(x, logits, k, lw, residual_bits=x, shared=sw)
+    got = oracle.bf16_to_f64(u16(xb))
+    expect = oracle.bf16_to_f64(ref["x_next"])
+    rel = np.linalg.norm(got - expect, axis=1) / np.linalg.norm(expect, axis=1)
+    assert rel.max() < ROW_REL_TOL, rel.max()
+    # the shared term is really there: without it the result is far off
+    plain = oracle.bf16_to_f64(oracle.layer_forward(x, logits, k, lw, residual_bits=x)["x_next"])
+    assert (np.linalg.norm(got - plain, axis=1) / np.linalg.norm(plain, axis=1)).max() > 1e-2
+
+
+def test_glm_decode_t8_with_shared_expert(glm_layer):
+    mq = _mq()
+    c = synth.CONFIGS[2]
+    x = synth.make_x(2, c.T, c.H)
+    logits = synth.make_logits(2, c.T, c.E)
+    sw = synth.make_shared(2, c.H, c.I)
+    L = mq.MoeLayer(c.T, c.H, c.I, c.E, c.k, shared_I=c.I)
+    y = L.forward(dev(x.view(np.int16)), dev(logits), mq.DeviceWeights.from_host(glm_layer),
+                  shared=mq.DeviceWeights.from_host(sw))
+    ref = oracle.layer_forward(x, logits, c.k, glm_layer, shared=sw)
+    rel = row_rel(u16(y), ref["y"])
+    assert np.all(np.isfinite(rel)) and rel.max() <= ROW_REL_TOL, rel.max()
