@@ -42,9 +42,17 @@ Readings where the pages are silent (each is listed with its reason in the desig
   everything else accumulates in fp64;
 * shared expert: a SwiGLU MLP of the routed experts' shape and storage format, run on every
   token with weight 1 and added to the routed sum before the residual (the usual
-  shared-expert MoE; the pages give its tensors and size, not the sum).
+  shared-expert MoE; the pages give its tensors and size, not the sum);
+* encoding: nearest magnitude with ties to the lower index, the sign bit for negative
+  weights only, exponents clamped to [-127, 127], all-zero blocks at byte 0, blocks with a
+  non-finite weight at byte 255 with zero codes; the grid fit takes its ratios (the data)
+  with the block exponents of the starting table and moves the levels by weighted Lloyd
+  rounds on them (an empty cell keeps its magnitude); the arm choice keeps the fitted grid
+  on a tie.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -52,7 +60,8 @@ __all__ = [
     "bf16_to_f64", "rne_bf16", "total_order_key", "router_logits", "route_topk",
     "permute_by_expert",
     "unpack_codes", "dequant_bf16", "layer_forward", "shared_expert_forward", "stack_forward",
-    "E2M1_TABLE",
+    "block_scale_bytes", "rtn_encode", "reconstruction_sq_error", "lloyd_stats",
+    "lloyd_update", "fit_grid", "select_arms", "E2M1_TABLE",
 ]
 
 # [card] "What this is": the MXFP4 (E2M1) magnitudes, one per 3-bit magnitude index.
@@ -229,6 +238,134 @@ def dequant_bf16(codes, scales, table) -> np.ndarray:
 
 def _expert_dense(codes, scales, table):
     return bf16_to_f64(dequant_bf16(codes, scales, table))
+
+
+# ----------------------------------------------------------------------------------------------
+# encoding (the quantizer) and the grid fit
+# ----------------------------------------------------------------------------------------------
+
+def block_scale_bytes(w_bits, gmax: float) -> np.ndarray:
+    """Scale byte of every block of 32 along K of bf16 weights [..., K].
+
+    [card] "Codes are indices into the per-layer grid": the grid is not amax-normalised, the
+    codes were packed against gmax * 2^e >= amax; the byte is e + 127 for the smallest such
+    integer e. Readings: e is clamped to [-127, 127]; an all-zero block gets byte 0; a block
+    holding an Inf or NaN gets byte 255 (it decodes to NaN).
+    """
+    w = bf16_to_f64(w_bits)
+    blocks = w.reshape(w.shape[:-1] + (w.shape[-1] // 32, 32))
+    out = np.empty(blocks.shape[:-1], np.uint8)
+    g = float(np.float32(gmax))
+    for idx in np.ndindex(out.shape):
+        b = blocks[idx]
+        if not np.all(np.isfinite(b)):
+            out[idx] = 255
+            continue
+        amax = float(np.max(np.abs(b)))
+        if amax == 0.0:
+            out[idx] = 0
+            continue
+        e = math.frexp(amax / g)[1]
+        while math.ldexp(g, e) < amax:
+            e += 1
+        while math.ldexp(g, e - 1) >= amax:
+            e -= 1
+        out[idx] = min(max(e, -127), 127) + 127
+    return out
+
+
+def rtn_encode(w_bits, table):
+    """Round-to-nearest encoding of bf16 weights [N, K] against 8 ascending magnitudes.
+
+    [card] "Codes are indices into the per-layer grid" (bits 0..2 index the grid, bit 3 is the
+    sign, w = sign * grid[mag] * 2^(s - 127)) and "Contents" (block 32 along K, two codes per
+    byte, the even K in the low nibble). Each weight takes the magnitude nearest to
+    |w| / 2^e, ties to the lower index (reading); bit 3 is set for negative weights (reading:
+    -0 keeps a clear sign bit). Returns codes uint8 [N, K/2], scales uint8 [N, K/32].
+    """
+    tab = np.asarray(table, dtype=np.float32).astype(np.float64)
+    w = bf16_to_f64(w_bits)
+    N, K = w.shape
+    scales = block_scale_bytes(w_bits, tab[7])
+    e = np.repeat(scales.astype(np.int64), 32, axis=1) - 127
+    r = np.abs(w) * np.ldexp(1.0, -e)                 # exact: a power-of-two rescale
+    mid = 0.5 * (tab[:-1] + tab[1:])                  # exact in fp64
+    mag = np.zeros((N, K), np.int64)
+    for i in range(7):
+        mag += r > mid[i]
+    codes4 = (mag | np.where(w < 0, 8, 0)).astype(np.uint8)
+    bad = np.repeat(scales == 255, 32, axis=1)
+    codes4[bad] = 0
+    packed = (codes4[:, 0::2] | (codes4[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scales
+
+
+def reconstruction_sq_error(w_bits, codes, scales, table) -> np.ndarray:
+    """Per row: sum over K of (w - w_hat)^2 in fp64, w_hat the bf16 dequantisation."""
+    w = bf16_to_f64(w_bits)
+    wh = bf16_to_f64(dequant_bf16(codes, scales, table))
+    return np.sum((w - wh) ** 2, axis=1)
+
+
+def lloyd_stats(w_bits, table, gmax=None):
+    """One weighted Lloyd-Max step's sums over bf16 weights [N, K] for 8 ascending magnitudes.
+
+    [card] "What this is": per-layer 8-magnitude codebooks fitted by weighted Lloyd-Max over
+    the pooled ratios |W / 2^e| of all experts' gate, up and down weights, each ratio weighted
+    by (2^e)^2 (its share of weight-space squared error). e is each block's exponent for the
+    top magnitude gmax (block_scale_bytes; default table[7]) and each ratio goes to its
+    nearest magnitude of `table` (the rtn_encode rule). Returns float64 [3, 8]: per magnitude
+    m, sum (2^e)^2 r, sum (2^e)^2 and sum (2^e)^2 (r - table[m])^2 over the ratios it holds.
+    Blocks with a non-finite weight are skipped.
+    """
+    tab = np.asarray(table, dtype=np.float32).astype(np.float64)
+    w = bf16_to_f64(w_bits)
+    scales = block_scale_bytes(w_bits, tab[7] if gmax is None else gmax)
+    keep = np.repeat(scales != 255, 32, axis=1)
+    e = np.repeat(scales.astype(np.int64), 32, axis=1) - 127
+    r = np.abs(w) * np.ldexp(1.0, -e)
+    mid = 0.5 * (tab[:-1] + tab[1:])
+    mag = np.zeros(w.shape, np.int64)
+    for i in range(7):
+        mag += r > mid[i]
+    wt = np.ldexp(1.0, 2 * e)
+    out = np.zeros((3, 8), np.float64)
+    for m in range(8):
+        sel = keep & (mag == m)
+        out[0, m] = np.sum(wt[sel] * r[sel])
+        out[1, m] = np.sum(wt[sel])
+        out[2, m] = np.sum(wt[sel] * (r[sel] - tab[m]) ** 2)
+    return out
+
+
+def lloyd_update(table, stats) -> np.ndarray:
+    """The next table: each magnitude moves to the weighted mean of its ratios (a magnitude
+    that holds no ratio stays), rounded to fp32."""
+    tab = np.asarray(table, dtype=np.float32).astype(np.float64)
+    s1, s0 = stats[0], stats[1]
+    new = np.where(s0 > 0, s1 / np.where(s0 > 0, s0, 1.0), tab)
+    return new.astype(np.float32)
+
+
+def fit_grid(mats, table0, iters: int):
+    """Weighted Lloyd-Max over the pooled ratios of several bf16 matrices: the ratios and their
+    weights are fixed by table0's top magnitude (the data of the fit), then iters rounds of
+    assignment and update (lloyd_stats summed over the matrices, lloyd_update) move the
+    levels; the weighted squared error of the ratios never goes up. Returns the fp32 table
+    (the matrices are then encoded against it, with its own top magnitude)."""
+    tab = np.asarray(table0, dtype=np.float32)
+    g0 = float(tab[7])
+    for _ in range(iters):
+        st = sum(lloyd_stats(m, tab, gmax=g0) for m in mats)
+        tab = lloyd_update(tab, st)
+    return tab
+
+
+def select_arms(err_a, err_b) -> np.ndarray:
+    """Per expert, arm 0 (the fitted grid) unless arm 1 (E2M1) has the strictly smaller
+    reconstruction error ([card] "Provenance": the winner is chosen per expert against an
+    E2M1 control arm). err_*: float64 [E]. Returns table ids uint8 [E]."""
+    return (np.asarray(err_b) < np.asarray(err_a)).astype(np.uint8)
 
 
 # ----------------------------------------------------------------------------------------------

@@ -481,3 +481,160 @@ def test_shared_expert_token_subset(tiny):
     np.testing.assert_array_equal(part["y"][[3, 11]], full["y"][[3, 11]])
     np.testing.assert_array_equal(part["shared_z"][[3, 11]], full["shared_z"][[3, 11]])
     assert not part["y"][0].any()
+
+
+# ----------------------------------------------------------------------------------------------
+# encoding (quantizer) and the weighted grid fit
+# ----------------------------------------------------------------------------------------------
+
+def _bits(a):
+    return synth.bf16_bits_from_f32(np.asarray(a, np.float32))
+
+
+def test_block_scale_closed_forms():
+    g = synth.lloyd_grid(1, 0)
+    gmax = float(g[7])
+    row = np.zeros((6, 32), np.float32)
+    row[0, 5] = 6.0                       # E2M1: amax = gmax * 2^0 exactly
+    row[1, 5] = np.float32(6.0 * 2 ** -9)                  # amax = gmax * 2^-9
+    row[2, 7] = np.nextafter(np.float32(6.0 * 2 ** -9), np.float32(1))  # just above (bf16 below)
+    row[3, 0] = np.inf
+    row[4, 3] = np.nan
+    bits = _bits(row)
+    bits[2, 7] = _bits([6.0 * 2 ** -9])[0] + 1             # the next bf16 above 6 * 2^-9
+    s = oracle.block_scale_bytes(bits, 6.0)[:, 0]
+    assert s.tolist() == [127, 118, 119, 255, 255, 0]
+    # the smallest e with gmax * 2^e >= amax, on the Lloyd grid's gmax
+    w = oracle.bf16_to_f64(_bits(np.random.default_rng(2).standard_normal((50, 32)) * 0.02))
+    sb = oracle.block_scale_bytes(_bits(w), gmax)[:, 0].astype(int) - 127
+    amax = np.abs(w).max(1)
+    assert np.all(gmax * 2.0 ** sb >= amax) and np.all(gmax * 2.0 ** (sb - 1) < amax)
+    # clamps: far below 2^-127 * gmax gets byte 0
+    tiny = np.zeros((1, 32), np.uint16)
+    tiny[0, 0] = 1                                          # the smallest bf16 subnormal
+    assert oracle.block_scale_bytes(tiny, gmax)[0, 0] == 0
+
+
+def _brute_codes(w_bits, scales, table):
+    """Nearest of the 16 codes, each decoded by the pinned decoder at the block's scale; ties
+    to the lower magnitude, then to the sign of w (negative only for w < 0)."""
+    w = oracle.bf16_to_f64(w_bits)
+    N, K = w.shape
+    values = {}
+    out = np.empty((N, K), np.uint8)
+    for n in range(N):
+        for k in range(K):
+            s = int(scales[n, k // 32])
+            if s not in values:
+                values[s] = [oracle.dequant_f64_exact(np.full((1, 16), c | (c << 4), np.uint8),
+                                                      np.array([[s]], np.uint8), table)[0, 0]
+                             for c in range(16)]
+            vals = values[s]
+            neg = bool(w[n, k] < 0)
+            out[n, k] = min(range(16), key=lambda c: (abs(w[n, k] - vals[c]), c & 7,
+                                                      bool(c & 8) != neg))
+    return out
+
+
+@pytest.mark.parametrize("which", ["lloyd", "e2m1"])
+def test_rtn_encode_matches_bruteforce_and_decoder(which):
+    table = synth.lloyd_grid(1, 0) if which == "lloyd" else oracle.E2M1_TABLE
+    g = np.random.default_rng(3)
+    w = (g.standard_normal((6, 128)) * 0.02).astype(np.float32)
+    w[0, :32] = 0.0                                         # all-zero block
+    w[1, 32:64] = (np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 4) *
+                   np.tile([1, -1], 16))                    # E2M1 midpoints: exact ties
+    w[2, 0] = -0.0
+    bits = _bits(w)
+    codes, scales = oracle.rtn_encode(bits, table)
+    c4 = oracle.unpack_codes(codes)
+    dec = oracle.dequant_f64_exact
+    assert np.array_equal(scales, oracle.block_scale_bytes(bits, table[7]))
+    want = _brute_codes(bits, scales, table)
+    np.testing.assert_array_equal(c4, want)
+    # round trip: each weight within half the largest gap (or the top overshoot) of the grid
+    wh = dec(codes, scales, table)
+    tab = np.asarray(table, np.float64)
+    half = max(np.max(np.diff(tab)) / 2, tab[0])
+    e = np.repeat(scales.astype(int) - 127, 32, axis=1)
+    assert np.all(np.abs(oracle.bf16_to_f64(bits) - wh) <= half * 2.0 ** e + 1e-300)
+    if which == "e2m1":
+        # midpoints tie to the lower magnitude
+        np.testing.assert_array_equal(c4[1, 32:40] & 7, [0, 1, 2, 3, 4, 5, 6, 7])
+
+
+@pytest.mark.parametrize("which", ["lloyd", "e2m1"])
+def test_rtn_encode_matches_generator_encoder(which):
+    """The input generator's C encoder (written separately, on fp32 input) agrees on weights
+    that are bf16 values."""
+    table = synth.lloyd_grid(2, 1) if which == "lloyd" else synth.E2M1_GRID
+    w = oracle.bf16_to_f64(_bits(synth.normal_matrix(synth.key(9, 2), 16, 512))).astype(np.float32)
+    c1, s1 = synth.rtn_encode(w, table)
+    c2, s2 = oracle.rtn_encode(_bits(w), table)
+    np.testing.assert_array_equal(s1, s2)
+    np.testing.assert_array_equal(c1, c2)
+
+
+def test_reconstruction_error_and_arm_selection():
+    g = np.random.default_rng(6)
+    lloyd = synth.lloyd_grid(1, 0)
+    gauss = _bits(g.standard_normal((32, 256)) * 0.02)
+    # weights exactly on the E2M1 grid (block maxima 6 * 2^e): E2M1 reconstructs them exactly
+    on = (oracle.E2M1_TABLE[g.integers(0, 8, (32, 256))] * np.where(g.random((32, 256)) < .5, -1, 1)
+          * 2.0 ** -8).astype(np.float32)
+    on[:, ::32] = 6 * 2.0 ** -8
+    on = _bits(on)
+    errs = {}
+    for name, w in (("gauss", gauss), ("on", on)):
+        for arm, tab in ((0, lloyd), (1, oracle.E2M1_TABLE)):
+            c, s = oracle.rtn_encode(w, tab)
+            e = oracle.reconstruction_sq_error(w, c, s, tab)
+            wh = oracle.bf16_to_f64(oracle.dequant_bf16(c, s, tab))
+            np.testing.assert_allclose(e, ((oracle.bf16_to_f64(w) - wh) ** 2).sum(1), rtol=1e-15)
+            errs[name, arm] = e.sum()
+    assert errs["on", 1] == 0.0 and errs["on", 0] > 0
+    assert errs["gauss", 0] < errs["gauss", 1]             # the fitted grid wins on Gaussians
+    ids = oracle.select_arms([errs["gauss", 0], errs["on", 0], 1.0],
+                             [errs["gauss", 1], errs["on", 1], 1.0])
+    assert ids.tolist() == [0, 1, 0]                       # a tie keeps the fitted grid
+
+
+def test_lloyd_stats_closed_form():
+    tab = oracle.E2M1_TABLE
+    w = np.zeros((1, 64), np.float32)
+    w[0, :4] = [6.0, 1.0, -1.0, 0.6]                    # e = 0: ratios 6, 1, 1, 0.6 (-> 0.5)
+    w[0, 32:35] = [24.0, -4.0, 1.0]                     # e = 2: ratios 6, 1, 0.25 (tie -> 0)
+    st = oracle.lloyd_stats(_bits(w), tab)
+    r06 = float(oracle.bf16_to_f64(_bits([0.6]))[0])
+    # level 0 holds 28 zeros at weight 1, 29 zeros and 0.25 at weight 16
+    np.testing.assert_allclose(st[:, 0], [16 * 0.25, 28 + 30 * 16, 16 * 0.25 ** 2], rtol=1e-15)
+    np.testing.assert_allclose(st[:, 1], [r06, 1, (r06 - 0.5) ** 2], rtol=1e-15)
+    np.testing.assert_allclose(st[:, 2], [2 + 16, 2 + 16, 0], rtol=1e-15)
+    np.testing.assert_allclose(st[:, 7], [6 + 16 * 6, 1 + 16, 0], rtol=1e-15)
+
+
+def test_weighted_lloyd_step_matches_sklearn_kmeans():
+    """One update equals one iteration of scikit-learn's weighted k-means (Lloyd) on the
+    ratios, started from the table, with the (2^e)^2 weights as sample weights."""
+    from sklearn.cluster import KMeans
+    g = np.random.default_rng(7)
+    w = g.standard_normal((24, 256)) * 0.02 * np.exp(g.standard_normal((24, 1)))
+    bits = _bits(w)
+    tab = synth.lloyd_grid(1, 0)
+    st = oracle.lloyd_stats(bits, tab)
+    assert np.all(st[1] > 0)                              # no empty cell (sklearn would move it)
+    new = oracle.lloyd_update(tab, st)
+    e = np.repeat(oracle.block_scale_bytes(bits, tab[7]).astype(int) - 127, 32, axis=1)
+    r = (np.abs(oracle.bf16_to_f64(bits)) * 2.0 ** -e).reshape(-1, 1)
+    km = KMeans(n_clusters=8, init=np.asarray(tab, np.float64).reshape(-1, 1), n_init=1,
+                max_iter=1, algorithm="lloyd", tol=0.0)
+    km.fit(r, sample_weight=(2.0 ** (2 * e)).ravel())
+    np.testing.assert_allclose(new, np.sort(km.cluster_centers_.ravel()).astype(np.float32),
+                               rtol=1e-6)
+    # on its fixed ratios (exponents of the starting table) the weighted distortion of the
+    # fit never goes up, round by round
+    d = [st[2].sum()]
+    for it in range(1, 5):
+        fitted = oracle.fit_grid([bits], tab, it)
+        d.append(oracle.lloyd_stats(bits, fitted, gmax=tab[7])[2].sum())
+    assert all(b <= a * (1 + 1e-12) for a, b in zip(d, d[1:])) and d[-1] < d[0]
