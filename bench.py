@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--shared", action="store_true",
                     help="layer workloads: add a shared expert (the routed experts' shape and "
                          "format, every token, weight 1) on a side stream, summed in the combine")
+    ap.add_argument("--encode", action="store_true",
+                    help="time the on-GPU encoder instead: weighted grid fit, per-expert arm "
+                         "choice and packing of one GLM-shaped layer of bf16 experts")
     ap.add_argument("--router", action="store_true",
                     help="stack: route every layer from its activations through a bf16 router "
                          "(logits = X . Wr^T, sigmoid gating) instead of pre-drawn logits")
@@ -252,6 +255,83 @@ def run_stack(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def run_encode(args):
+    """The on-GPU encoder on one GLM-shaped layer: 256 experts of bf16 N(0, 0.02) gate, up
+    [2048, 6144] and down [6144, 2048] drawn on the device (19.3 GB). One step = two rounds of
+    the weighted grid fit (moeq_lloyd_stats over the three matrices), the two error passes per
+    matrix for the arm choice (moeq_quantize without output bytes, moeq_select_arms) and the
+    packing pass (moeq_quantize with codes and scales): 9 passes over the weights."""
+    import torch
+    import codebook_quantized_moe_amd as mq
+    from codebook_quantized_moe_amd import encode
+    import synth
+
+    E, H, I = 256, 6144, 2048
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.key(2, 98))
+    mats = []
+    for shape in ((E, I, H), (E, I, H), (E, H, I)):
+        m = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        for e in range(E):
+            m[e].normal_(0.0, 0.02, generator=gen)
+        mats.append(m.view(torch.int16))
+    wbytes = sum(m.numel() * 2 for m in mats)
+    g0 = synth.lloyd_grid(2, 0)
+    # warm-up on one expert
+    encode.fit_grid([m[:1] for m in mats], g0, 1)
+    encode.encode_layer(*[m[:1] for m in mats], g0)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    grid, dist = encode.fit_grid(mats, g0, 2)
+    ev[1].record()
+    enc = encode.encode_layer(*mats, grid)
+    ev[2].record()
+    torch.cuda.synchronize()
+    fit_ms = ev[0].elapsed_time(ev[1])
+    enc_ms = ev[1].elapsed_time(ev[2])
+    total_ms = fit_ms + enc_ms
+    # one packing pass alone, for the kernel's own rate
+    q0 = torch.cuda.Event(enable_timing=True)
+    q1 = torch.cuda.Event(enable_timing=True)
+    m = mats[0]
+    codes = torch.empty((E, I, H // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((E, I, H // 32), dtype=torch.uint8, device=dev)
+    q0.record()
+    mq.moeq_quantize(m, E, I, H, enc["tables"], enc["table_id"], codes, scales, None)
+    q1.record()
+    torch.cuda.synchronize()
+    q_ms = q0.elapsed_time(q1)
+    q_bytes = m.numel() * 2 + codes.numel() + scales.numel()
+    ach = q_bytes / (q_ms / 1e3) / 1e9
+    tid = enc["table_id"].cpu().numpy()
+    out = {
+        "metric": "layer encode: bf16 GB/s over the 9 passes (grid fit, arm choice, packing)",
+        "value": round(9 * wbytes / (total_ms / 1e3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": 1,
+        "warmup": 1,
+        "ms_per_step": round(total_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (N(0, 0.02) drawn on the device)",
+        "config": {"workload": "glm_layer_encode", "experts": E, "hidden": H, "intermediate": I,
+                   "weight_bytes": wbytes, "fit_rounds": 2},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "quantize_kernel (packing pass of the gate matrices)"},
+        "encode": {"fit_ms": round(fit_ms, 2), "arms_and_pack_ms": round(enc_ms, 2),
+                   "grid": [round(float(v), 5) for v in grid],
+                   "fit_weighted_sq_error": dist, "experts_on_e2m1": int(tid.sum())},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -263,6 +343,8 @@ def main():
     import codebook_quantized_moe_amd as mq
     import synth
 
+    if args.encode:
+        return run_encode(args)
     cfg = synth.CONFIGS[args.config]
     if cfg.layers > 1:
         return run_stack(args, cfg)

@@ -33,7 +33,8 @@ MAX_TABLES = 4
 EXPORTED = ("moeq_last_error", "moeq_workspace_bytes", "moeq_router_logits", "moeq_route_topk",
             "moeq_permute_by_expert", "moeq_gateup_swiglu", "moeq_down",
             "moeq_unpermute_combine", "moeq_shared_workspace_bytes", "moeq_shared_expert",
-            "moeq_unpermute_combine_shared", "moeq_debug_dequant")
+            "moeq_unpermute_combine_shared", "moeq_quantize", "moeq_lloyd_workspace_bytes",
+            "moeq_lloyd_stats", "moeq_select_arms", "moeq_debug_dequant")
 
 _i, _vp, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
 _lib.moeq_last_error.restype = ctypes.c_char_p
@@ -61,6 +62,15 @@ _lib.moeq_shared_expert.argtypes = [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _v
                                     _vp, _vp, _vp, _sz, _vp]
 _lib.moeq_unpermute_combine_shared.restype = _i
 _lib.moeq_unpermute_combine_shared.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]
+_ll, _f = ctypes.c_longlong, ctypes.c_float
+_lib.moeq_quantize.restype = _i
+_lib.moeq_quantize.argtypes = [_vp, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp]
+_lib.moeq_lloyd_workspace_bytes.restype = _sz
+_lib.moeq_lloyd_workspace_bytes.argtypes = [_i, _i]
+_lib.moeq_lloyd_stats.restype = _i
+_lib.moeq_lloyd_stats.argtypes = [_vp, _i, _i, _i, _vp, _f, _i, _vp, _vp, _sz, _vp]
+_lib.moeq_select_arms.restype = _i
+_lib.moeq_select_arms.argtypes = [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]
 _lib.moeq_debug_dequant.restype = _i
 _lib.moeq_debug_dequant.argtypes = [_vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _vp]
 
@@ -168,6 +178,28 @@ def moeq_unpermute_combine_shared(yp, pair_pos, expert_offsets, T, k, E, H, shar
     _check(_lib.moeq_unpermute_combine_shared(_p(yp), _p(pair_pos), _p(expert_offsets), T, k, E,
                                               H, _p(shared_z), _p(residual), _p(y),
                                               _stream(stream)))
+
+
+def moeq_quantize(w, E, N, K, tables, table_id, codes, scales, row_err, stream=None):
+    tab, n = _tables(tables)
+    _check(_lib.moeq_quantize(_p(w), E, N, K, tab.ctypes.data, n, _p(table_id), _p(codes),
+                              _p(scales), _p(row_err), _stream(stream)))
+
+
+def moeq_lloyd_workspace_bytes(E: int, N: int) -> int:
+    return int(_lib.moeq_lloyd_workspace_bytes(E, N))
+
+
+def moeq_lloyd_stats(w, E, N, K, table, gmax, accumulate, stats, ws, ws_bytes, stream=None):
+    tab = np.ascontiguousarray(np.asarray(table, dtype=np.float32).reshape(8))
+    _check(_lib.moeq_lloyd_stats(_p(w), E, N, K, tab.ctypes.data, float(gmax),
+                                 1 if accumulate else 0, _p(stats), _p(ws), ws_bytes,
+                                 _stream(stream)))
+
+
+def moeq_select_arms(err_a, err_b, E, N, accumulate, table_id, expert_err, stream=None):
+    _check(_lib.moeq_select_arms(_p(err_a), _p(err_b), E, N, 1 if accumulate else 0,
+                                 _p(table_id), _p(expert_err), _stream(stream)))
 
 
 def moeq_debug_dequant(codes, scales, E, N, K, tables, table_id, out, stream=None):

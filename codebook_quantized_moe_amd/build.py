@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoeq.so")
 
-SOURCES = ["api.hip", "router.hip", "route.hip", "permute.hip", "gemm_decode.hip", "gemm_prefill.hip", "dequant.hip", "combine.hip"]
+SOURCES = ["api.hip", "quantize.hip", "router.hip", "route.hip", "permute.hip", "gemm_decode.hip", "gemm_prefill.hip", "dequant.hip", "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CLANGXX = "/opt/rocm/llvm/bin/clang++"

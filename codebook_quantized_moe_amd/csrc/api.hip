@@ -339,6 +339,79 @@ int moeq_shared_expert(const uint16_t* x, int T, int H, int I, const uint8_t* ga
                       (hipStream_t)stream);
 }
 
+static int check_ascending(const char* w, const float* table, int t) {
+    for (int m = 1; m < 8; ++m)
+        if (!(table[m] >= table[m - 1]))
+            return fail(MOEQ_EINVAL, "%s: table %d must be non-decreasing (entry %d < entry %d)", w,
+                        t, m, m - 1);
+    if (!(table[7] > 0.0f))
+        return fail(MOEQ_EINVAL, "%s: table %d has no positive magnitude", w, t);
+    return MOEQ_OK;
+}
+
+int moeq_quantize(const uint16_t* wts, int E, int N, int K, const float* tables, int n_tables,
+                  const uint8_t* table_id, uint8_t* codes, uint8_t* scales, double* row_err,
+                  void* stream) {
+    const char* w = "moeq_quantize";
+    if (E < 1 || N < 1 || K < 32) return fail(MOEQ_EINVAL, "%s: bad sizes E=%d N=%d K=%d", w, E, N, K);
+    if (K % 32) return fail(MOEQ_EUNSUPPORTED, "%s: K = %d must be a multiple of 32", w, K);
+    TableArgs ta;
+    if (int r = check_tables(w, tables, n_tables, &ta)) return r;
+    for (int t = 0; t < n_tables; ++t)
+        if (int r = check_ascending(w, tables + 8 * t, t)) return r;
+    if (!wts || !table_id) return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    if (!aligned(wts, 16) || (codes && !aligned(codes, 16)) || (row_err && !aligned(row_err, 8)))
+        return fail(MOEQ_EUNSUPPORTED, "%s: w and codes must be 16-byte aligned, row_err 8-byte aligned", w);
+    if ((long long)E * N >= (1LL << 33)) return fail(MOEQ_EUNSUPPORTED, "%s: too many rows", w);
+    clear_hip_error();
+    launch_quantize(wts, (long long)E * N, K, N, ta, table_id, codes, scales, row_err,
+                    (hipStream_t)stream);
+    return check_launch(w);
+}
+
+size_t moeq_lloyd_workspace_bytes(int E, int N) {
+    if (E < 1 || N < 1) return 0;
+    return lloyd_workspace_bytes((long long)E * N);
+}
+
+int moeq_lloyd_stats(const uint16_t* wts, int E, int N, int K, const float* table, float gmax,
+                     int accumulate, double* stats, void* ws, size_t ws_bytes, void* stream) {
+    const char* w = "moeq_lloyd_stats";
+    if (E < 1 || N < 1 || K < 32) return fail(MOEQ_EINVAL, "%s: bad sizes E=%d N=%d K=%d", w, E, N, K);
+    if (K % 32) return fail(MOEQ_EUNSUPPORTED, "%s: K = %d must be a multiple of 32", w, K);
+    TableArgs ta;
+    if (int r = check_tables(w, table, 1, &ta)) return r;
+    if (int r = check_ascending(w, table, 0)) return r;
+    if (!(gmax > 0.0f) || !isfinite(gmax)) return fail(MOEQ_EINVAL, "%s: gmax = %g must be positive and finite", w, (double)gmax);
+    if (!wts || !stats) return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    const size_t need = moeq_lloyd_workspace_bytes(E, N);
+    if (!ws || ws_bytes < need)
+        return fail(MOEQ_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", w, need, ws_bytes);
+    if (!aligned(wts, 16) || !aligned(stats, 8) || !aligned(ws, 8))
+        return fail(MOEQ_EUNSUPPORTED, "%s: w must be 16-byte aligned, stats and ws 8-byte aligned", w);
+    if ((long long)E * N >= (1LL << 33)) return fail(MOEQ_EUNSUPPORTED, "%s: too many rows", w);
+    Table8 tab;
+    for (int m = 0; m < 8; ++m) tab.v[m] = table[m];
+    clear_hip_error();
+    launch_lloyd_stats(wts, (long long)E * N, K, tab, gmax, static_cast<double*>(ws),
+                       accumulate ? 1 : 0, stats, (hipStream_t)stream);
+    return check_launch(w);
+}
+
+int moeq_select_arms(const double* err_a, const double* err_b, int E, int N, int accumulate,
+                     uint8_t* table_id, double* expert_err, void* stream) {
+    const char* w = "moeq_select_arms";
+    if (E < 1 || N < 1) return fail(MOEQ_EINVAL, "%s: bad sizes E=%d N=%d", w, E, N);
+    if (!err_a || !err_b || !table_id || (accumulate && !expert_err))
+        return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    if (!aligned(err_a, 8) || !aligned(err_b, 8) || (expert_err && !aligned(expert_err, 8)))
+        return fail(MOEQ_EUNSUPPORTED, "%s: error arrays must be 8-byte aligned", w);
+    clear_hip_error();
+    launch_select_arms(err_a, err_b, E, N, accumulate ? 1 : 0, table_id, expert_err,
+                       (hipStream_t)stream);
+    return check_launch(w);
+}
+
 int moeq_debug_dequant(const uint8_t* codes, const uint8_t* scales, int E, int N, int K,
                        const float* tables, int n_tables, const uint8_t* table_id, uint16_t* out,
                        void* stream) {

@@ -48,6 +48,18 @@ void launch_pair_split_rows(const uint16_t* x, int T, int H, uint16_t* xs, int c
 void launch_combine(const float* yp, const int32_t* pair_pos, const int32_t* offsets, int T, int k,
                     int E, int H, const float* shared_z, const uint16_t* residual, uint16_t* y,
                     hipStream_t stream);
+// encoding and grid fit
+struct Table8 {
+    float v[8];
+};
+void launch_quantize(const uint16_t* w, long long rows, int K, int N, const TableArgs& ta,
+                     const uint8_t* table_id, uint8_t* codes, uint8_t* scales, double* row_err,
+                     hipStream_t stream);
+size_t lloyd_workspace_bytes(long long rows);
+void launch_lloyd_stats(const uint16_t* w, long long rows, int K, const Table8& tab, float gmax,
+                        double* part, int accumulate, double* stats, hipStream_t stream);
+void launch_select_arms(const double* err_a, const double* err_b, int E, int N, int accumulate,
+                        uint8_t* table_id, double* expert_err, hipStream_t stream);
 // shared expert: routing of every token to one expert with weight 1, in the workspace
 inline size_t shared_rows_bytes(int T) { return ((size_t)T * 4 + 255) / 256 * 256; }
 inline size_t shared_routing_bytes(int T) { return 256 + 2 * shared_rows_bytes(T); }

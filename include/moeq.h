@@ -242,6 +242,61 @@ int moeq_unpermute_combine_shared(const float* yp, const int32_t* pair_pos,
                                   void* stream);
 
 /*
+ * Encode bf16 expert weights into the 4-bit format (GLM-5.2-NF4-Lloyd-Experts-GPTQ model card,
+ * "Codes are indices into the per-layer grid": the grid is not amax-normalised; a block of 32
+ * weights along K is packed against gmax * 2^e >= amax and stores the byte e + 127; "Contents":
+ * two codes per byte, the even K in the low nibble). Per block: e is the smallest integer with
+ * table[7] * 2^e >= max |w| (clamped to [-127, 127]; an all-zero block gets byte 0, a block
+ * holding an Inf or NaN gets byte 255 and zero codes); per weight: bits 0..2 index the
+ * magnitude nearest to |w| / 2^e (ties to the lower index; decided exactly), bit 3 is set for
+ * w < 0 (not for -0).
+ *   w        bf16 [E, N, K] device, 16-byte aligned, K a multiple of 32
+ *   tables   HOST fp32 [n_tables][8], 1 <= n_tables <= MOEQ_MAX_TABLES: finite magnitudes,
+ *            non-decreasing, table[7] > 0
+ *   table_id uint8 [E] device: the table of each expert (an id >= n_tables encodes NaN blocks)
+ *   codes    uint8 [E, N, K/2] out, 16-byte aligned, or NULL
+ *   scales   uint8 [E, N, K/32] out, or NULL
+ *   row_err  fp64 [E * N] out, 8-byte aligned, or NULL: per row, sum over K of
+ *            (w - bf16 dequantisation)^2 in fp64 (NaN when a block has byte 255)
+ * Errors: MOEQ_EINVAL for bad sizes, null pointers or tables; MOEQ_EUNSUPPORTED for K not a
+ * multiple of 32 or misalignment. Nothing is allocated.
+ */
+int moeq_quantize(const uint16_t* w, int E, int N, int K, const float* tables, int n_tables,
+                  const uint8_t* table_id, uint8_t* codes, uint8_t* scales, double* row_err,
+                  void* stream);
+
+/*
+ * One step of the weighted Lloyd-Max grid fit (the model card, "What this is": 8 magnitudes
+ * per layer fitted over the pooled ratios |W / 2^e| of all experts' gate, up and down weights,
+ * each ratio weighted by (2^e)^2). Over the bf16 weights [E, N, K]: e per block for the top
+ * magnitude gmax (the moeq_quantize rule), each ratio r = |w| / 2^e assigned to its nearest
+ * entry of `table` (ties to the lower), and per entry m the fp64 sums
+ *     stats[m] = sum (2^e)^2 r,  stats[8 + m] = sum (2^e)^2,  stats[16 + m] = sum (2^e)^2 (r - table[m])^2
+ * Blocks holding an Inf or NaN are skipped. The next table is stats[m] / stats[8 + m] (keep
+ * table[m] where the sum of weights is 0). With accumulate != 0 the sums are added to stats
+ * (pooling several calls, in call order), else they overwrite it. Summation order is fixed.
+ *   table  HOST fp32 [8], finite, non-decreasing, table[7] > 0; gmax > 0 finite
+ *   stats  fp64 [24] device
+ *   ws     moeq_lloyd_workspace_bytes(E, N) bytes, 8-byte aligned (per-workgroup partial sums)
+ * Errors as for moeq_quantize; MOEQ_EWORKSPACE for a missing or short workspace.
+ */
+size_t moeq_lloyd_workspace_bytes(int E, int N);
+int moeq_lloyd_stats(const uint16_t* w, int E, int N, int K, const float* table, float gmax,
+                     int accumulate, double* stats, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Per-expert choice between two encodings (the model card, "Provenance": each expert's winner
+ * is chosen against an E2M1 control arm): err_a, err_b fp64 [E * N] row errors of one matrix
+ * of every expert from moeq_quantize under two tables. Per expert the two sums over its N rows
+ * (row order) are written to expert_err [2E] (a, b), or added to it with accumulate != 0 (the
+ * gate, up and down matrices of the experts in three calls); table_id[e] = 1 when the second
+ * total is strictly smaller, else 0. expert_err may be NULL only without accumulate.
+ * Errors: MOEQ_EINVAL for bad sizes or null pointers.
+ */
+int moeq_select_arms(const double* err_a, const double* err_b, int E, int N, int accumulate,
+                     uint8_t* table_id, double* expert_err, void* stream);
+
+/*
  * Test entry point: decode whole matrices with the same device decode path the two
  * projections use (model card, "Codes are indices into the per-layer grid").
  *   codes uint8 [E, N, K/2], scales uint8 [E, N, K/32], out bf16 [E, N, K] (natural K order)

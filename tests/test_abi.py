@@ -201,3 +201,37 @@ def test_shared_expert_contract():
     assert _status(f, None, FAKE, FAKE, 8, 8, 256, 6144, FAKE, None, FAKE,
                    stream=0) == mq.MOEQ_EINVAL
     f(None, None, None, 0, 8, 256, 6144, None, None, None, stream=0)   # T = 0: no-op, OK
+
+
+def test_quantizer_validation():
+    q = mq.moeq_quantize
+    ok = dict(w=FAKE, E=2, N=4, K=64, tables=GOOD_TABLES, table_id=FAKE, codes=FAKE, scales=FAKE,
+              row_err=FAKE, stream=0)
+    bad = [
+        (dict(K=48), mq.MOEQ_EUNSUPPORTED),
+        (dict(K=16), mq.MOEQ_EINVAL),
+        (dict(E=0), mq.MOEQ_EINVAL),
+        (dict(w=None), mq.MOEQ_EINVAL),
+        (dict(table_id=None), mq.MOEQ_EINVAL),
+        (dict(codes=FAKE + 8), mq.MOEQ_EUNSUPPORTED),
+        (dict(row_err=FAKE + 4), mq.MOEQ_EUNSUPPORTED),
+        (dict(tables=np.array([[0, .5, 1, 1.5, 2, 3, 6, 4]], np.float32)), mq.MOEQ_EINVAL),
+        (dict(tables=np.zeros((1, 8), np.float32)), mq.MOEQ_EINVAL),
+    ]
+    for over, code in bad:
+        a = dict(ok)
+        a.update(over)
+        assert _status(q, **a) == code, over
+    assert "non-decreasing" in mq.moeq_last_error() or "positive" in mq.moeq_last_error()
+    ls = mq.moeq_lloyd_stats
+    need = mq.moeq_lloyd_workspace_bytes(2, 4)
+    assert need == 2 * 24 * 8                  # 8 rows: 2 workgroups of 24 fp64 sums
+    assert _status(ls, FAKE, 2, 4, 64, GOOD_TABLES[0], 0.0, 0, FAKE, FAKE, need,
+                   stream=0) == mq.MOEQ_EINVAL                        # gmax must be > 0
+    assert _status(ls, FAKE, 2, 4, 64, GOOD_TABLES[0], 2.73, 0, FAKE, FAKE, need - 1,
+                   stream=0) == mq.MOEQ_EWORKSPACE
+    assert _status(ls, FAKE, 2, 4, 64, GOOD_TABLES[0], 2.73, 0, None, FAKE, need,
+                   stream=0) == mq.MOEQ_EINVAL
+    sa = mq.moeq_select_arms
+    assert _status(sa, FAKE, FAKE, 0, 4, 0, FAKE, None, stream=0) == mq.MOEQ_EINVAL
+    assert _status(sa, FAKE, FAKE, 2, 4, 1, FAKE, None, stream=0) == mq.MOEQ_EINVAL  # accumulate

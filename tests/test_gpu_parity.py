@@ -549,3 +549,152 @@ def test_glm_decode_t8_with_shared_expert(glm_layer):
     ref = oracle.layer_forward(x, logits, c.k, glm_layer, shared=sw)
     rel = row_rel(u16(y), ref["y"])
     assert np.all(np.isfinite(rel)) and rel.max() <= ROW_REL_TOL, rel.max()
+
+
+# ----------------------------------------------------------------------------------------------
+# encoding (quantizer), grid fit and arm choice
+# ----------------------------------------------------------------------------------------------
+
+def _special_weights(seed, E, N, K):
+    """bf16 bits [E, N, K]: N(0, 0.02) with scale spread per row, plus blocks that exercise
+    the rules: all zero, exact E2M1 midpoint ties, -0, subnormals, huge values, Inf/NaN."""
+    g = np.random.default_rng(seed)
+    w = (g.standard_normal((E, N, K)) * 0.02 * np.exp(g.standard_normal((E, N, 1)))).astype(np.float32)
+    w[0, 0, :32] = 0.0
+    w[0, 1, :32] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 4) * np.tile([1, -1], 16)
+    w[0, 2, 5] = -0.0
+    w[0, 3, 32:64] = np.float32(1e-39) * g.standard_normal(32).astype(np.float32)   # subnormal
+    w[0, 4, :32] *= 1e30
+    bits = synth.bf16_bits_from_f32(w)
+    bits[0, 5, 40] = 0x7F80                      # +Inf
+    bits[0, 6, 70] = 0xFFC1                      # NaN
+    return bits
+
+
+def test_quantize_bitexact():
+    mq = _mq()
+    E, N, K = 3, 40, 256
+    bits = _special_weights(51, E, N, K)
+    tables = np.stack([synth.lloyd_grid(1, 0), oracle.E2M1_TABLE]).astype(np.float32)
+    tid = np.array([0, 1, 0], np.uint8)
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device="cuda")
+    err = torch.empty(E * N, dtype=torch.float64, device="cuda")
+    mq.moeq_quantize(dev(bits.view(np.int16)), E, N, K, tables, dev(tid), codes, scales, err)
+    gc, gs, ge = host(codes), host(scales), host(err).reshape(E, N)
+    for e in range(E):
+        tab = tables[tid[e]]
+        rc, rs = oracle.rtn_encode(bits[e], tab)
+        np.testing.assert_array_equal(gs[e], rs)
+        np.testing.assert_array_equal(gc[e], rc)
+        re = oracle.reconstruction_sq_error(bits[e], rc, rs, tab)
+        np.testing.assert_array_equal(np.isnan(ge[e]), np.isnan(re))
+        ok = ~np.isnan(re)
+        np.testing.assert_allclose(ge[e][ok], re[ok], rtol=1e-12, atol=1e-300)
+    assert gs[0, 5, 1] == 255 and gs[0, 6, 2] == 255 and gs[0, 0, 0] == 0
+    # a second call gives the same bytes; codes-only and error-only calls agree with the full one
+    err2 = torch.empty_like(err)
+    mq.moeq_quantize(dev(bits.view(np.int16)), E, N, K, tables, dev(tid), None, None, err2)
+    np.testing.assert_array_equal(host(err2).view(np.uint64), host(err).view(np.uint64))
+
+
+def test_quantize_invalid_table_id_gives_nan_blocks():
+    mq = _mq()
+    E, N, K = 2, 8, 96
+    bits = _special_weights(52, E, N, K)
+    codes = torch.full((E, N, K // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device="cuda")
+    err = torch.empty(E * N, dtype=torch.float64, device="cuda")
+    mq.moeq_quantize(dev(bits.view(np.int16)), E, N, K, oracle.E2M1_TABLE[None],
+                     dev(np.array([0, 3], np.uint8)), codes, scales, err)
+    assert (host(scales)[1] == 255).all() and (host(codes)[1] == 0).all()
+    assert np.isnan(host(err)[N:]).all()
+
+
+def test_lloyd_stats_and_pooling():
+    mq = _mq()
+    tab = synth.lloyd_grid(1, 0)
+    mats = [_special_weights(53, 2, 24, 192), _special_weights(54, 3, 16, 256)]
+    stats = torch.empty(24, dtype=torch.float64, device="cuda")
+    ref = np.zeros((3, 8))
+    for i, m in enumerate(mats):
+        E, N, K = m.shape
+        need = mq.moeq_lloyd_workspace_bytes(E, N)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        mq.moeq_lloyd_stats(dev(m.view(np.int16)), E, N, K, tab, 2.5, i > 0, stats, ws, need)
+        ref += sum(oracle.lloyd_stats(m[e], tab, gmax=2.5) for e in range(E))
+    np.testing.assert_allclose(host(stats).reshape(3, 8), ref, rtol=1e-12)
+
+
+def test_grid_fit_and_layer_encode_end_to_end(path):
+    """Fit the grid (weighted Lloyd), choose arms and encode a layer on the GPU; then run the
+    encoded layer forward on the GPU: all against the oracle."""
+    from codebook_quantized_moe_amd import encode
+    mq = _mq()
+    T, E, H, I, k = 24, 6, 256, 128, 2
+    g = np.random.default_rng(55)
+    def draw(shape):
+        return synth.bf16_bits_from_f32(g.standard_normal(shape) * 0.02)
+    gate, up, down = draw((E, I, H)), draw((E, I, H)), draw((E, H, I))
+    # expert 4: weights exactly on the E2M1 grid, so E2M1 reconstructs it exactly
+    for m in (gate, up, down):
+        vals = oracle.E2M1_TABLE[g.integers(0, 8, m.shape[1:])] * np.where(
+            g.random(m.shape[1:]) < .5, -1, 1) * 2.0 ** -8
+        vals[:, ::32] = 6 * 2.0 ** -8
+        m[4] = synth.bf16_bits_from_f32(vals)
+    mats = [dev(m.view(np.int16)) for m in (gate, up, down)]
+    g0 = synth.lloyd_grid(1, 0)
+    grid, dist = encode.fit_grid(mats, g0, 3)
+    ref_grid = oracle.fit_grid([m[e] for m in (gate, up, down) for e in range(E)], g0, 3)
+    np.testing.assert_allclose(grid, ref_grid, rtol=1e-6)
+    assert all(b <= a * (1 + 1e-12) for a, b in zip(dist, dist[1:]))
+    enc = encode.encode_layer(*mats, grid)
+    # arms and bytes, decided by the oracle on the GPU's own grid
+    errs = np.zeros((E, 2))
+    for m in (gate, up, down):
+        for e in range(E):
+            for t, tb in enumerate((grid, oracle.E2M1_TABLE)):
+                c, s = oracle.rtn_encode(m[e], tb)
+                errs[e, t] += oracle.reconstruction_sq_error(m[e], c, s, tb).sum()
+    np.testing.assert_allclose(host(enc["expert_err"]), errs, rtol=1e-12)
+    tid = oracle.select_arms(errs[:, 0], errs[:, 1])
+    np.testing.assert_array_equal(host(enc["table_id"]), tid)
+    assert tid[4] == 1 and tid.sum() == 1
+    lw = synth.LayerWeights(*(np.empty(0),) * 6, tables=enc["tables"], table_id=tid)
+    for name, m in (("gate", gate), ("up", up), ("down", down)):
+        cs = [oracle.rtn_encode(m[e], enc["tables"][tid[e]]) for e in range(E)]
+        np.testing.assert_array_equal(host(enc[name + "_codes"]), np.stack([c for c, _ in cs]))
+        np.testing.assert_array_equal(host(enc[name + "_scales"]), np.stack([s for _, s in cs]))
+        setattr(lw, name + "_codes", np.stack([c for c, _ in cs]))
+        setattr(lw, name + "_scales", np.stack([s for _, s in cs]))
+    # the encoded layer through the forward path
+    x = synth.make_x(55, T, H)
+    logits = synth.make_logits(55, T, E)
+    w = mq.DeviceWeights(enc["gate_codes"], enc["gate_scales"], enc["up_codes"],
+                         enc["up_scales"], enc["down_codes"], enc["down_scales"],
+                         enc["tables"], enc["table_id"])
+    L = mq.MoeLayer(T, H, I, E, k)
+    y = L.forward(dev(x.view(np.int16)), dev(logits), w)
+    ref = oracle.layer_forward(x, logits, k, lw)
+    rel = row_rel(u16(y), ref["y"])
+    assert rel.max() <= ROW_REL_TOL, rel.max()
+
+
+def test_quantize_glm_expert_sampled_rows():
+    """A GLM-size expert matrix (2048 x 6144) in the launch the layer encoder uses; sampled
+    rows against the oracle."""
+    mq = _mq()
+    N, K = 2048, 6144
+    bits = synth.bf16_bits_from_f32(synth.normal_matrix(synth.key(56, 1), N, K))
+    tables = np.stack([synth.lloyd_grid(2, 0), oracle.E2M1_TABLE]).astype(np.float32)
+    codes = torch.empty((1, N, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((1, N, K // 32), dtype=torch.uint8, device="cuda")
+    err = torch.empty(N, dtype=torch.float64, device="cuda")
+    mq.moeq_quantize(dev(bits.view(np.int16)), 1, N, K, tables, dev(np.zeros(1, np.uint8)),
+                     codes, scales, err)
+    rows = [0, 1, 777, 2047]
+    rc, rs = oracle.rtn_encode(bits[rows], tables[0])
+    np.testing.assert_array_equal(host(codes)[0, rows], rc)
+    np.testing.assert_array_equal(host(scales)[0, rows], rs)
+    np.testing.assert_allclose(host(err)[rows], oracle.reconstruction_sq_error(bits[rows], rc, rs, tables[0]),
+                               rtol=1e-12)
