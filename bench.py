@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2,
                     help="tokens of the workload the CPU oracle is timed on")
+    ap.add_argument("--fused", action="store_true",
+                    help="decode workloads: the whole layer as one cooperative launch "
+                         "(moeq_moe_decode) instead of the five per-step calls")
     ap.add_argument("--shared", action="store_true",
                     help="layer workloads: add a shared expert (the routed experts' shape and "
                          "format, every token, weight 1) on a side stream, summed in the combine")
@@ -73,6 +76,11 @@ KERNEL_SOURCES = {
                             "codebook_quantized_moe_amd/csrc/moeq_device.h"],
     "prefill_kernel<true>": ["codebook_quantized_moe_amd/csrc/gemm_prefill.hip",
                              "codebook_quantized_moe_amd/csrc/moeq_device.h"],
+    "decode_layer_kernel": ["codebook_quantized_moe_amd/csrc/gemm_decode.hip",
+                            "codebook_quantized_moe_amd/csrc/moeq_device.h",
+                            "codebook_quantized_moe_amd/csrc/route_device.h",
+                            "codebook_quantized_moe_amd/csrc/permute_device.h",
+                            "codebook_quantized_moe_amd/csrc/combine_device.h"],
 }
 
 
@@ -383,8 +391,18 @@ def main():
         off = L.offsets.cpu().numpy()
         touched.append(int((np.diff(off) > 0).sum()))
 
+    fused = args.fused and decode and sw is None
+
     def step(b, ev=None):
         w = copies[b % ncopies]
+        if fused:
+            if ev is not None:
+                ev[b][0].record()
+            L.forward_fused(xd[b], ld[b], w)
+            if ev is not None:
+                ev[b][1].record()
+                ev[b][2].record()
+            return
         if sw is not None:
             # the shared expert on the side stream, beside the routed path
             main = torch.cuda.current_stream()
@@ -450,7 +468,14 @@ def main():
     gu_avg = float(np.mean(gu_ms))
     kernel = "decode_kernel<true>" if decode else "prefill_kernel<true>"
     traffic = profiled_traffic(kernel, cfg.name)
-    if decode:
+    if fused:
+        # one kernel for the whole layer: its algorithmic bytes over its duration
+        kernel = "decode_layer_kernel"
+        traffic = profiled_traffic(kernel, cfg.name)
+        ach = float(np.mean(step_bytes)) / (gu_avg / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+    elif decode:
         ach = float(np.mean(gu_bytes)) / (gu_avg / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
@@ -477,9 +502,13 @@ def main():
         "config": {"workload": cfg.name, "tokens": T, "hidden": H, "intermediate": I,
                    "experts": E, "top_k": k, "zipf_s": cfg.zipf_s,
                    "e2m1_experts": list(cfg.e2m1), "channel_permutation": cfg.permute,
-                   "weight_copies": ncopies, "shared_expert": sw is not None},
+                   "weight_copies": ncopies, "shared_expert": sw is not None,
+                   "single_launch": fused},
         "roofline": roof,
-        "kernels": {
+        "kernels": {"decode_layer": {"avg_us": round(gu_avg * 1e3, 2),
+                                     "bytes_per_launch": int(np.mean(step_bytes)),
+                                     "GB_s": round(float(np.mean(step_bytes)) / gu_avg / 1e6, 1)}}
+        if fused else {
             "gateup_swiglu": {"avg_us": round(gu_avg * 1e3, 2),
                               "bytes_per_launch": int(np.mean(gu_bytes)),
                               "GB_s": round(float(np.mean(gu_bytes)) / gu_avg / 1e6, 1),

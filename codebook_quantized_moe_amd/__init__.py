@@ -34,7 +34,8 @@ EXPORTED = ("moeq_last_error", "moeq_workspace_bytes", "moeq_router_logits", "mo
             "moeq_permute_by_expert", "moeq_gateup_swiglu", "moeq_down",
             "moeq_unpermute_combine", "moeq_shared_workspace_bytes", "moeq_shared_expert",
             "moeq_unpermute_combine_shared", "moeq_quantize", "moeq_lloyd_workspace_bytes",
-            "moeq_lloyd_stats", "moeq_select_arms", "moeq_debug_dequant")
+            "moeq_lloyd_stats", "moeq_select_arms", "moeq_moe_decode_workspace_bytes",
+            "moeq_moe_decode", "moeq_moe_decode_check", "moeq_debug_dequant")
 
 _i, _vp, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
 _lib.moeq_last_error.restype = ctypes.c_char_p
@@ -71,6 +72,13 @@ _lib.moeq_lloyd_stats.restype = _i
 _lib.moeq_lloyd_stats.argtypes = [_vp, _i, _i, _i, _vp, _f, _i, _vp, _vp, _sz, _vp]
 _lib.moeq_select_arms.restype = _i
 _lib.moeq_select_arms.argtypes = [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]
+_lib.moeq_moe_decode_workspace_bytes.restype = _sz
+_lib.moeq_moe_decode_workspace_bytes.argtypes = [_i] * 5
+_lib.moeq_moe_decode.restype = _i
+_lib.moeq_moe_decode.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moeq_moe_decode_check.restype = _i
+_lib.moeq_moe_decode_check.argtypes = [_vp, _vp]
 _lib.moeq_debug_dequant.restype = _i
 _lib.moeq_debug_dequant.argtypes = [_vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _vp]
 
@@ -200,6 +208,24 @@ def moeq_lloyd_stats(w, E, N, K, table, gmax, accumulate, stats, ws, ws_bytes, s
 def moeq_select_arms(err_a, err_b, E, N, accumulate, table_id, expert_err, stream=None):
     _check(_lib.moeq_select_arms(_p(err_a), _p(err_b), E, N, 1 if accumulate else 0,
                                  _p(table_id), _p(expert_err), _stream(stream)))
+
+
+def moeq_moe_decode_workspace_bytes(T: int, k: int, E: int, H: int, I: int) -> int:
+    return int(_lib.moeq_moe_decode_workspace_bytes(T, k, E, H, I))
+
+
+def moeq_moe_decode(x, logits, T, H, I, E, k, gate_codes, gate_scales, up_codes, up_scales,
+                    down_codes, down_scales, tables, table_id, residual, y, ws, ws_bytes,
+                    gating=MOEQ_GATING_SOFTMAX_TOPK, stream=None):
+    tab, n = _tables(tables)
+    _check(_lib.moeq_moe_decode(_p(x), _p(logits), T, H, I, E, k, gating, _p(gate_codes),
+                                _p(gate_scales), _p(up_codes), _p(up_scales), _p(down_codes),
+                                _p(down_scales), tab.ctypes.data, n, _p(table_id), _p(residual),
+                                _p(y), _p(ws), ws_bytes, _stream(stream)))
+
+
+def moeq_moe_decode_check(ws, stream=None):
+    _check(_lib.moeq_moe_decode_check(_p(ws), _stream(stream)))
 
 
 def moeq_debug_dequant(codes, scales, E, N, K, tables, table_id, out, stream=None):

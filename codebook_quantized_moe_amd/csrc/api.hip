@@ -339,6 +339,30 @@ int moeq_shared_expert(const uint16_t* x, int T, int H, int I, const uint8_t* ga
                       (hipStream_t)stream);
 }
 
+// Workspace of moeq_moe_decode, in 256-byte aligned regions.
+struct DecodeWs {
+    size_t bar, ids, w, offsets, sorted_pair, pair_pos, xs, inter, yp, total;
+};
+
+static size_t up256(size_t n) { return (n + 255) / 256 * 256; }
+
+static DecodeWs decode_ws(int T, int k, int E, int H, int I) {
+    DecodeWs d;
+    const size_t P = (size_t)T * k;
+    size_t o = 0;
+    d.bar = o;          o += 256;
+    d.ids = o;          o += up256(P * 4);
+    d.w = o;            o += up256(P * 4);
+    d.offsets = o;      o += up256((size_t)(E + 1) * 4);
+    d.sorted_pair = o;  o += up256(P * 4);
+    d.pair_pos = o;     o += up256(P * 4);
+    d.xs = o;           o += up256((size_t)T * H * 2);
+    d.inter = o;        o += up256(P * I * 2);
+    d.yp = o;           o += up256(P * H * 4);
+    d.total = o;
+    return d;
+}
+
 static int check_ascending(const char* w, const float* table, int t) {
     for (int m = 1; m < 8; ++m)
         if (!(table[m] >= table[m - 1]))
@@ -410,6 +434,109 @@ int moeq_select_arms(const double* err_a, const double* err_b, int E, int N, int
     launch_select_arms(err_a, err_b, E, N, accumulate ? 1 : 0, table_id, expert_err,
                        (hipStream_t)stream);
     return check_launch(w);
+}
+
+size_t moeq_moe_decode_workspace_bytes(int T, int k, int E, int H, int I) {
+    if (T <= 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0) return 0;
+    return decode_ws(T, k, E, H, I).total;
+}
+
+int moeq_moe_decode(const uint16_t* x, const float* logits, int T, int H, int I, int E, int k,
+                    int gating, const uint8_t* gate_codes, const uint8_t* gate_scales,
+                    const uint8_t* up_codes, const uint8_t* up_scales, const uint8_t* down_codes,
+                    const uint8_t* down_scales, const float* tables, int n_tables,
+                    const uint8_t* table_id, const uint16_t* residual, uint16_t* y, void* ws,
+                    size_t ws_bytes, void* stream) {
+    const char* w = "moeq_moe_decode";
+    if (int r = check_sizes(w, T, k, E)) return r;
+    if (gating != MOEQ_GATING_SOFTMAX_TOPK && gating != MOEQ_GATING_SIGMOID_TOPK)
+        return fail(MOEQ_EINVAL, "%s: unknown gating %d", w, gating);
+    if (T == 0) return ok();
+    if ((long long)T * k > kDecodeMaxRows)
+        return fail(MOEQ_EUNSUPPORTED, "%s: T * k = %lld above %lld rows (use the per-step calls)",
+                    w, (long long)T * k, kDecodeMaxRows);
+    if (!x || !logits || !y) return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    if (!aligned(y, 8) || (residual && !aligned(residual, 8)))
+        return fail(MOEQ_EUNSUPPORTED, "%s: y and residual must be 8-byte aligned", w);
+    const DecodeWs d = decode_ws(T, k, E, H, I);
+    if (!ws || ws_bytes < d.total)
+        return fail(MOEQ_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", w, d.total, ws_bytes);
+    if (!aligned(ws, 256)) return fail(MOEQ_EUNSUPPORTED, "%s: the workspace must be 256-byte aligned", w);
+    uint8_t* b = static_cast<uint8_t*>(ws);
+    DecodeLayerArgs L;
+    memset(&L, 0, sizeof(L));
+    L.barrier = reinterpret_cast<int*>(b + d.bar);
+    L.ids = reinterpret_cast<int32_t*>(b + d.ids);
+    L.w = reinterpret_cast<float*>(b + d.w);
+    L.offsets = reinterpret_cast<int32_t*>(b + d.offsets);
+    L.sorted_pair = reinterpret_cast<int32_t*>(b + d.sorted_pair);
+    L.pair_pos = reinterpret_cast<int32_t*>(b + d.pair_pos);
+    uint16_t* xs = reinterpret_cast<uint16_t*>(b + d.xs);
+    uint16_t* inter = reinterpret_cast<uint16_t*>(b + d.inter);
+    float* yp = reinterpret_cast<float*>(b + d.yp);
+    // both projections validated as the per-step calls would (their workspace is unused here)
+    const size_t pws = moeq_workspace_bytes(T, k, E, H, I);
+    if (int r = projection(w, true, x, T, H, I, E, k, L.offsets, L.sorted_pair, nullptr,
+                           gate_codes, gate_scales, up_codes, up_scales, tables, n_tables, table_id,
+                           inter, ws, pws, (hipStream_t)stream, false))
+        return r;
+    if (int r = projection(w, false, inter, T, H, I, E, k, L.offsets, L.sorted_pair, L.w,
+                           down_codes, down_scales, nullptr, nullptr, tables, n_tables, table_id,
+                           yp, ws, pws, (hipStream_t)stream, false))
+        return r;
+    auto fill = [&](SkinnyArgs& a, bool gateup) {
+        if (int r = check_tables(w, tables, n_tables, &a.tables)) return r;
+        a.offsets = L.offsets;
+        a.sorted_pair = L.sorted_pair;
+        a.table_id = table_id;
+        a.T = T;
+        a.k = k;
+        a.E = E;
+        if (gateup) {
+            a.act = xs;
+            a.act_bytes = (uint32_t)((long long)T * H * 2);
+            a.codes0 = gate_codes; a.scales0 = gate_scales;
+            a.codes1 = up_codes; a.scales1 = up_scales;
+            a.out = inter;
+            a.N = I; a.K = H; a.out_ld = I;
+        } else {
+            a.act = inter;
+            a.act_bytes = (uint32_t)((long long)T * k * I * 2);
+            a.topk_w = L.w;
+            a.codes0 = down_codes; a.scales0 = down_scales;
+            a.out = yp;
+            a.N = H; a.K = I; a.out_ld = H;
+        }
+        return (int)MOEQ_OK;
+    };
+    if (int r = fill(L.gu, true)) return r;
+    if (int r = fill(L.dn, false)) return r;
+    L.logits = logits;
+    L.sigmoid = gating == MOEQ_GATING_SIGMOID_TOPK ? 1 : 0;
+    L.x = reinterpret_cast<const u32x4*>(x);
+    L.xs = reinterpret_cast<u32x4*>(xs);
+    L.x_units = (long)T * H / 8;
+    L.yp = yp;
+    L.residual = residual;
+    L.y = y;
+    L.T = T; L.k = k; L.E = E; L.H = H;
+    clear_hip_error();
+    const int g = launch_decode_layer(L, cu_count(), (hipStream_t)stream);
+    if (g < 0) return fail(MOEQ_ELAUNCH, "%s: the cooperative launch was refused (%d)", w, g);
+    return check_launch(w);
+}
+
+int moeq_moe_decode_check(const void* ws, void* stream) {
+    const char* w = "moeq_moe_decode_check";
+    if (!ws) return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    int flag = 0;
+    clear_hip_error();
+    if (hipMemcpyAsync(&flag, static_cast<const uint8_t*>(ws) + 4, sizeof(int),
+                       hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess ||
+        hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+        return fail(MOEQ_ELAUNCH, "%s: reading the barrier word failed", w);
+    if (flag) return fail(MOEQ_ELAUNCH, "%s: a grid barrier of the last call gave up waiting", w);
+    return ok();
 }
 
 int moeq_debug_dequant(const uint8_t* codes, const uint8_t* scales, int E, int N, int K,

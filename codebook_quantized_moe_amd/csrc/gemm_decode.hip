@@ -27,8 +27,11 @@
 // down ("Round 7" brief, decision 6; README "What had to be fixed": router weighting in the
 // down epilogue): writes topk_w[p] * (I . Wd) in fp32.
 // The grid is persistent; expert row counts are read from expert_offsets on the device.
+#include "combine_device.h"
 #include "moeq_device.h"
 #include "moeq_kernels.h"
+#include "permute_device.h"
+#include "route_device.h"
 
 #include <algorithm>
 
@@ -173,14 +176,13 @@ __device__ __forceinline__ int weight_row(int cb, int w, int g, int q, int* mat)
     return cb * S::kRowsPerWG + w * 16 + g * 4 + q;
 }
 
+// One projection over the whole persistent grid (every workgroup calls it; it returns when
+// the workgroup's items are done). smem: the launch's dynamic LDS; meta: LDS for the item map.
 template <bool GATEUP, class S>
-__global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
-decode_kernel(const SkinnyArgs a) {
+__device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, ExpertMeta& meta) {
     constexpr int kChunkK = S::kChunkK, kRowsPerWG = S::kRowsPerWG;
     constexpr int kARowUnits = S::kARowUnits, kABufBytes = S::kABufBytes;
     constexpr int kSBufBytes = S::kSBufBytes, kSRowBytes = S::kSRowBytes;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    __shared__ ExpertMeta meta;
     u32x4* tab = reinterpret_cast<u32x4*>(smem);
     uint8_t* abuf = smem + (size_t)a.tables.n * 256 * 16;
     uint8_t* sbuf = abuf + 2 * kABufBytes;
@@ -433,6 +435,14 @@ decode_kernel(const SkinnyArgs a) {
     }
 }
 
+template <bool GATEUP, class S>
+__global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+decode_kernel(const SkinnyArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ ExpertMeta meta;
+    decode_body<GATEUP, S>(a, smem, meta);
+}
+
 template <class S>
 static void launch_shape(const SkinnyArgs& a, bool gateup, long items, int cus, hipStream_t stream) {
     const size_t lds = (size_t)a.tables.n * 256 * 16 + 2 * S::kABufBytes + 2 * S::kSBufBytes +
@@ -459,6 +469,108 @@ void launch_decode(const SkinnyArgs& a, bool gateup, long tiles, int cus, int sh
     case 4: launch_shape<DecShape<16, 2048>>(a, gateup, items(gateup ? 128 : 256), cus, stream); break;
     default: launch_shape<DecShape<8, 2048>>(a, gateup, items(gateup ? 64 : 128), cus, stream); break;
     }
+}
+
+// ---------------------------------------------------------------------------------------------
+// The whole decode layer in one cooperative launch: routing and permutation (workgroup 0) beside
+// the pair-split copy of x (the other workgroups), gate|up, down, combine, with a grid barrier
+// between phases. The grid is co-resident (a cooperative launch fails rather than run it
+// otherwise). A barrier gives up after about a second of waiting and records that in the
+// barrier word, so a broken barrier ends the kernel instead of hanging it.
+// ---------------------------------------------------------------------------------------------
+constexpr int kBarrierSpinLimit = 1 << 22;
+
+__device__ inline void grid_barrier(int* bar, int target) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();                          // this workgroup's writes before its arrival
+        __hip_atomic_fetch_add(&bar[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int spins = 0;
+        while (__hip_atomic_load(&bar[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(8);
+            if (++spins > kBarrierSpinLimit) {
+                __hip_atomic_fetch_or(&bar[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+        __threadfence();                          // the others' writes after the wait
+    }
+    __syncthreads();
+}
+
+template <class S>
+__global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+decode_layer_kernel(const DecodeLayerArgs L) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ ExpertMeta meta;
+    const int nwg = gridDim.x, tid = threadIdx.x;
+    const int P = L.T * L.k;
+    // workgroup 0 records when it starts and leaves each phase (64-bit constant-rate clock,
+    // 100 MHz) in the barrier header: bar[2 + 2 i], i = 0..4
+    auto stamp = [&](int i) {
+        if (blockIdx.x == 0 && tid == 0)
+            reinterpret_cast<unsigned long long*>(L.barrier)[1 + i] = __builtin_amdgcn_s_memrealtime();
+    };
+    stamp(0);
+    // phase 1
+    if (blockIdx.x == 0) {
+        for (int t = tid >> 6; t < L.T; t += S::kWaves)
+            route_token(L.logits, t, L.E, L.k, L.sigmoid != 0, L.ids, L.w);
+        __syncthreads();
+        permute_block<S::kWaves>(L.ids, P, L.E, L.offsets, L.sorted_pair, L.pair_pos);
+    }
+    if (blockIdx.x > 0 || nwg == 1) {
+        const long first = nwg == 1 ? tid : (long)(blockIdx.x - 1) * S::kThreads + tid;
+        const long step = (long)(nwg == 1 ? 1 : nwg - 1) * S::kThreads;
+        for (long i = first; i < L.x_units; i += step)
+            L.xs[i] = pair_split(__builtin_nontemporal_load(L.x + i));
+    }
+    grid_barrier(L.barrier, nwg);
+    stamp(1);
+    decode_body<true, S>(L.gu, smem, meta);
+    grid_barrier(L.barrier, 2 * nwg);
+    stamp(2);
+    decode_body<false, S>(L.dn, smem, meta);
+    grid_barrier(L.barrier, 3 * nwg);
+    stamp(3);
+    // phase 4: combine, 4 columns per thread
+    const int quads = L.H / 4;
+    const int valid = L.offsets[L.E];
+    for (long u = (long)blockIdx.x * S::kThreads + tid; u < (long)L.T * quads;
+         u += (long)nwg * S::kThreads) {
+        const int t = (int)(u / quads), h = (int)(u % quads) * 4;
+        combine_cols(L.yp, L.pair_pos, valid, t, h, L.k, L.H, nullptr, L.residual, L.y);
+    }
+    stamp(4);
+}
+
+__global__ void zero_barrier_kernel(int* bar) {
+    if (threadIdx.x < 2) bar[threadIdx.x] = 0;
+}
+
+// Launch geometry of the fused kernel: dynamic LDS and the largest co-resident grid.
+static size_t decode_layer_lds(const DecodeLayerArgs& L) {
+    using S = DecShape<8, 2048>;
+    return (size_t)L.gu.tables.n * 256 * 16 + 2 * S::kABufBytes + 2 * S::kSBufBytes +
+           (size_t)L.T * L.k * 4;
+}
+
+int launch_decode_layer(const DecodeLayerArgs& L, int cus, hipStream_t stream) {
+    using S = DecShape<8, 2048>;
+    const size_t lds = decode_layer_lds(L);
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_layer_kernel<S>, S::kThreads,
+                                                     lds) != hipSuccess || per_cu < 1)
+        return -1;
+    const int blocks = cus * per_cu;
+    hipLaunchKernelGGL(zero_barrier_kernel, dim3(1), dim3(64), 0, stream, L.barrier);
+    DecodeLayerArgs arg = L;
+    void* params[] = {&arg};
+    if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(decode_layer_kernel<S>),
+                                   dim3(blocks), dim3(S::kThreads), params, (unsigned)lds,
+                                   stream) != hipSuccess)
+        return -2;
+    return blocks;
 }
 
 }  // namespace moeq

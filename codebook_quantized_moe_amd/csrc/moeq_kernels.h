@@ -48,6 +48,28 @@ void launch_pair_split_rows(const uint16_t* x, int T, int H, uint16_t* xs, int c
 void launch_combine(const float* yp, const int32_t* pair_pos, const int32_t* offsets, int T, int k,
                     int E, int H, const float* shared_z, const uint16_t* residual, uint16_t* y,
                     hipStream_t stream);
+// the whole decode layer in one cooperative launch (gemm_decode.hip)
+struct DecodeLayerArgs {
+    SkinnyArgs gu, dn;            // the two projections (routing arrays inside the workspace)
+    const float* logits;          // [T, E]
+    int sigmoid;                  // gating: 0 softmax, 1 sigmoid
+    const u32x4* x;               // [T, H] bf16 as 16-byte units
+    u32x4* xs;                    // its pair-split copy
+    long x_units;                 // T * H / 8
+    int32_t* ids;                 // [T*k]
+    float* w;                     // [T*k]
+    int32_t* offsets;             // [E + 1]
+    int32_t* sorted_pair;         // [T*k]
+    int32_t* pair_pos;            // [T*k]
+    const float* yp;              // [T*k, H] (the down projection's output)
+    const uint16_t* residual;     // [T, H] or null
+    uint16_t* y;                  // [T, H]
+    int* barrier;                 // 2 ints: arrivals, failure flag
+    int T, k, E, H;
+};
+// returns the grid size, or < 0 when the cooperative launch was refused
+int launch_decode_layer(const DecodeLayerArgs& L, int cus, hipStream_t stream);
+
 // encoding and grid fit
 struct Table8 {
     float v[8];

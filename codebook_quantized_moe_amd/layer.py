@@ -11,7 +11,8 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from . import (MOEQ_GATING_SOFTMAX_TOPK, moeq_down, moeq_gateup_swiglu, moeq_permute_by_expert,
+from . import (MOEQ_GATING_SOFTMAX_TOPK, moeq_down, moeq_gateup_swiglu, moeq_moe_decode,
+               moeq_moe_decode_workspace_bytes, moeq_permute_by_expert,
                moeq_route_topk, moeq_router_logits, moeq_shared_expert,
                moeq_shared_workspace_bytes, moeq_unpermute_combine,
                moeq_unpermute_combine_shared, moeq_workspace_bytes)
@@ -145,6 +146,19 @@ class MoeLayer:
         if shared is not None:
             stream.wait_event(self.join)
         return self.combine(residual, out, stream, shared=shared is not None)
+
+    def forward_fused(self, x, logits, w: DeviceWeights, residual=None, out=None, stream=None):
+        """The decode layer as one cooperative launch (moeq_moe_decode); T * k <= 4096."""
+        if not hasattr(self, "f_ws"):
+            self.f_ws_bytes = moeq_moe_decode_workspace_bytes(self.T, self.k, self.E, self.H,
+                                                              self.I)
+            self.f_ws = torch.empty(self.f_ws_bytes, dtype=torch.uint8, device=self.y.device)
+        out = self.y if out is None else out
+        moeq_moe_decode(x, logits, self.T, self.H, self.I, self.E, self.k, w.gate_codes,
+                        w.gate_scales, w.up_codes, w.up_scales, w.down_codes, w.down_scales,
+                        w.tables, w.table_id, residual, out, self.f_ws, self.f_ws_bytes,
+                        gating=self.gating, stream=stream)
+        return out
 
     def forward_routed(self, x, router_w, w: DeviceWeights, residual=None, out=None,
                        stream=None, shared: DeviceWeights | None = None):

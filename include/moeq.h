@@ -242,6 +242,36 @@ int moeq_unpermute_combine_shared(const float* yp, const int32_t* pair_pos,
                                   void* stream);
 
 /*
+ * The whole few-rows (decode) layer in one cooperative launch: moeq_route_topk,
+ * moeq_permute_by_expert, moeq_gateup_swiglu, moeq_down and moeq_unpermute_combine with the
+ * same results, run as phases of one grid separated by grid barriers (README of
+ * GLM-5.2-EXL3-TR3v4-3.5bpw-MTP78, "Tuning" / "Why": one fused launch per layer, a grid the
+ * size of the machine; cutting launches gained decode throughput). Workgroup 0 routes and
+ * permutes while the others write the pair-split copy of x; then gate|up, down and the
+ * combine run on the whole grid.
+ *   x, logits, weights, tables, table_id, gating: as for the per-step calls
+ *   residual bf16 [T, H] or NULL; y bf16 [T, H] out (may be the residual buffer)
+ *   ws       moeq_moe_decode_workspace_bytes(T, k, E, H, I) bytes, 256-byte aligned: the
+ *            barrier words, routing arrays, pair-split x, intermediate and expert outputs
+ *            (scratch between calls; calls that overlap need their own). Bytes 8..47 receive
+ *            five 64-bit stamps of the device's constant 100 MHz clock, taken by workgroup 0
+ *            at the start and after each of the four phases (for profiling).
+ * Requires T * k <= 4096 (the few-rows kernels' limit). A grid barrier that waits more than
+ * about a second gives up instead of hanging and marks the call: moeq_moe_decode_check
+ * synchronizes the stream and reports it (MOEQ_ELAUNCH), as it reports nothing otherwise.
+ * Errors: as for the per-step calls; MOEQ_EUNSUPPORTED above 4096 rows; MOEQ_ELAUNCH when the
+ * device refuses the cooperative launch.
+ */
+size_t moeq_moe_decode_workspace_bytes(int T, int k, int E, int H, int I);
+int moeq_moe_decode(const uint16_t* x, const float* logits, int T, int H, int I, int E, int k,
+                    int gating, const uint8_t* gate_codes, const uint8_t* gate_scales,
+                    const uint8_t* up_codes, const uint8_t* up_scales, const uint8_t* down_codes,
+                    const uint8_t* down_scales, const float* tables, int n_tables,
+                    const uint8_t* table_id, const uint16_t* residual, uint16_t* y, void* ws,
+                    size_t ws_bytes, void* stream);
+int moeq_moe_decode_check(const void* ws, void* stream);
+
+/*
  * Encode bf16 expert weights into the 4-bit format (GLM-5.2-NF4-Lloyd-Experts-GPTQ model card,
  * "Codes are indices into the per-layer grid": the grid is not amax-normalised; a block of 32
  * weights along K is packed against gmax * 2^e >= amax and stores the byte e + 127; "Contents":

@@ -235,3 +235,31 @@ def test_quantizer_validation():
     sa = mq.moeq_select_arms
     assert _status(sa, FAKE, FAKE, 0, 4, 0, FAKE, None, stream=0) == mq.MOEQ_EINVAL
     assert _status(sa, FAKE, FAKE, 2, 4, 1, FAKE, None, stream=0) == mq.MOEQ_EINVAL  # accumulate
+
+
+def test_moe_decode_validation():
+    f = mq.moeq_moe_decode
+    need = mq.moeq_moe_decode_workspace_bytes(8, 8, 256, 6144, 2048)
+    assert need > 8 * 8 * 6144 * 4                       # holds the expert outputs
+    ok = dict(x=FAKE, logits=FAKE, T=8, H=6144, I=2048, E=256, k=8, gate_codes=FAKE,
+              gate_scales=FAKE, up_codes=FAKE, up_scales=FAKE, down_codes=FAKE, down_scales=FAKE,
+              tables=GOOD_TABLES, table_id=FAKE, residual=None, y=FAKE, ws=FAKE, ws_bytes=need,
+              stream=0)
+    bad = [
+        (dict(T=1024, ws_bytes=1 << 40), mq.MOEQ_EUNSUPPORTED),      # T * k above 4096 rows
+        (dict(ws_bytes=need - 1), mq.MOEQ_EWORKSPACE),
+        (dict(ws=FAKE + 16), mq.MOEQ_EUNSUPPORTED),
+        (dict(logits=None), mq.MOEQ_EINVAL),
+        (dict(gating=7), mq.MOEQ_EINVAL),
+        (dict(H=6000), mq.MOEQ_EUNSUPPORTED),
+        (dict(down_codes=None), mq.MOEQ_EINVAL),
+        (dict(E=300), mq.MOEQ_EINVAL),
+    ]
+    for over, code in bad:
+        a = dict(ok)
+        a.update(over)
+        assert _status(f, **a) == code, over
+    a = dict(ok)
+    a.update(T=0, x=None, ws=None, ws_bytes=0)
+    f(**a)                                                 # T = 0: no-op, OK
+    assert _status(mq.moeq_moe_decode_check, None, stream=0) == mq.MOEQ_EINVAL

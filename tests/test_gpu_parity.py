@@ -698,3 +698,42 @@ def test_quantize_glm_expert_sampled_rows():
     np.testing.assert_array_equal(host(scales)[0, rows], rs)
     np.testing.assert_allclose(host(err)[rows], oracle.reconstruction_sq_error(bits[rows], rc, rs, tables[0]),
                                rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------------------------
+# the decode layer as one cooperative launch
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,H,I,k,gating", [(16, 4, 256, 128, 2, 0), (37, 8, 576, 320, 4, 1),
+                                              (1, 16, 256, 128, 16, 0), (8, 256, 6144, 2048, 8, 0),
+                                              (64, 256, 6144, 2048, 8, 1)])
+def test_moe_decode_single_launch(T, E, H, I, k, gating, monkeypatch):
+    """Bit-identical to the per-step calls on the few-rows kernels (the same kernels' phases,
+    the same summation orders) and within the bar of the oracle; residual updated in place;
+    a second call with other inputs (the barrier word is reset per call)."""
+    monkeypatch.setenv("MOEQ_FORCE_PATH", "decode")
+    mq = _mq()
+    if H == 6144:
+        lw = synth.make_layer(2, E, H, I) if T == 8 else synth.make_layer(61, E, H, I)
+    else:
+        lw = synth.make_layer(61, E, H, I, e2m1_experts=(1,), permute="random")
+    w = mq.DeviceWeights.from_host(lw)
+    L = mq.MoeLayer(T, H, I, E, k, gating=gating)
+    for call in range(2):
+        x = synth.make_x(61, T, H, batch=call)
+        logits = synth.make_logits(61, T, E, batch=call)
+        xb, lg = dev(x.view(np.int16)), dev(logits)
+        ref_bits = u16(L.forward(xb, lg, w, residual=xb, out=torch.empty_like(xb)))
+        y = L.forward_fused(xb, lg, w, residual=xb, out=xb)            # in place over x
+        mq.moeq_moe_decode_check(L.f_ws)
+        np.testing.assert_array_equal(u16(y), ref_bits)
+        if H != 6144 or call == 0:
+            routing = oracle.route_topk(logits, k, "sigmoid" if gating else "softmax")
+            tokens = None if T <= 16 else list(range(0, T, 9))
+            ref = oracle.layer_forward(x, logits, k, lw, residual_bits=x, routing=routing,
+                                       tokens=tokens)
+            toks = np.arange(T) if tokens is None else np.asarray(tokens)
+            got = oracle.bf16_to_f64(u16(y))[toks]
+            expect = oracle.bf16_to_f64(ref["x_next"])[toks]
+            rel = np.linalg.norm(got - expect, axis=1) / np.linalg.norm(expect, axis=1)
+            assert rel.max() < ROW_REL_TOL, rel.max()
