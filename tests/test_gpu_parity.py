@@ -727,7 +727,9 @@ def test_moe_decode_single_launch(T, E, H, I, k, gating, monkeypatch):
         y = L.forward_fused(xb, lg, w, residual=xb, out=xb)            # in place over x
         mq.moeq_moe_decode_check(L.f_ws)
         np.testing.assert_array_equal(u16(y), ref_bits)
-        if H != 6144 or call == 0:
+        # the oracle on the small shapes and the 8-token GLM layer (the bit-identity above ties
+        # the rest to the per-step calls, which their own tests hold to the oracle)
+        if H != 6144 or (call == 0 and T <= 8):
             routing = oracle.route_topk(logits, k, "sigmoid" if gating else "softmax")
             tokens = None if T <= 16 else list(range(0, T, 9))
             ref = oracle.layer_forward(x, logits, k, lw, residual_bits=x, routing=routing,
