@@ -1,7 +1,8 @@
 """Benchmark of the routed-expert MoE layer forward over 4-bit codebook experts on one MI355X.
 
 One step = one pass of the whole hot path (route -> permute -> gate|up+SwiGLU -> down ->
-unpermute/combine) over one batch of synthetic tokens, with inputs resident in HBM.
+unpermute/combine; routing and permutation as one launch for few tokens) over one batch of
+synthetic tokens, with inputs resident in HBM.
 
 Default workload: the GLM-shaped single-layer decode (hidden 6144, intermediate 2048,
 256 experts, top-8, 8 tokens), HBM-bound. Every step routes a fresh batch of tokens, and the
@@ -170,9 +171,9 @@ def run_stack(args, cfg):
     def route(lg):
         if args.router:
             ML.router(X, lg)
-            ML.route(ML.logits)
+            ML.route_permute(ML.logits)
         else:
-            ML.route(lg)
+            ML.route_permute(lg)
 
     # touched experts per layer (with the router they follow the activations, which every
     # step starts again from x0, so one untimed pass gives them)
@@ -180,7 +181,6 @@ def run_stack(args, cfg):
     X.copy_(x0)
     for w, lg in layers:
         route(lg)
-        ML.permute()
         touched.append(int((np.diff(ML.offsets.cpu().numpy()) > 0).sum()))
         ML.gateup(X, w)
         ML.down(w)
@@ -196,7 +196,6 @@ def run_stack(args, cfg):
         X.copy_(x0)
         for l, (w, lg) in enumerate(layers):
             route(lg)
-            ML.permute()
             if timing:
                 ev[b][l][0].record()
             ML.gateup(X, w)
@@ -414,8 +413,7 @@ def main():
             if ev is not None:
                 ev[b][4].record(L.side)
             L.join.record(L.side)
-        L.route(ld[b])
-        L.permute()
+        L.route_permute(ld[b])
         if ev is not None:
             ev[b][0].record()
         L.gateup(xd[b], w)

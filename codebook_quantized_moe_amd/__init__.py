@@ -31,7 +31,7 @@ MAX_EXPERTS = 256
 MAX_TABLES = 4
 
 EXPORTED = ("moeq_last_error", "moeq_workspace_bytes", "moeq_router_logits", "moeq_route_topk",
-            "moeq_permute_by_expert", "moeq_gateup_swiglu", "moeq_down",
+            "moeq_permute_by_expert", "moeq_route_permute", "moeq_gateup_swiglu", "moeq_down",
             "moeq_unpermute_combine", "moeq_shared_workspace_bytes", "moeq_shared_expert",
             "moeq_unpermute_combine_shared", "moeq_quantize", "moeq_lloyd_workspace_bytes",
             "moeq_lloyd_stats", "moeq_select_arms", "moeq_moe_decode_workspace_bytes",
@@ -46,6 +46,8 @@ _lib.moeq_router_logits.restype = _i
 _lib.moeq_router_logits.argtypes = [_vp, _i, _i, _vp, _i, _vp, _vp]
 _lib.moeq_route_topk.restype = _i
 _lib.moeq_route_topk.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp, _vp]
+_lib.moeq_route_permute.restype = _i
+_lib.moeq_route_permute.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.moeq_permute_by_expert.restype = _i
 _lib.moeq_permute_by_expert.argtypes = [_vp, _i, _i, _i, _vp, _vp, _vp, _vp]
 _lib.moeq_gateup_swiglu.restype = _i
@@ -137,6 +139,13 @@ def moeq_route_topk(logits, T, E, k, topk_ids, topk_w, gating=MOEQ_GATING_SOFTMA
                     stream=None):
     _check(_lib.moeq_route_topk(_p(logits), T, E, k, gating, _p(topk_ids), _p(topk_w),
                                 _stream(stream)))
+
+
+def moeq_route_permute(logits, T, E, k, topk_ids, topk_w, expert_offsets, sorted_pair, pair_pos,
+                       gating=MOEQ_GATING_SOFTMAX_TOPK, stream=None):
+    _check(_lib.moeq_route_permute(_p(logits), T, E, k, gating, _p(topk_ids), _p(topk_w),
+                                   _p(expert_offsets), _p(sorted_pair), _p(pair_pos),
+                                   _stream(stream)))
 
 
 def moeq_permute_by_expert(topk_ids, T, k, E, expert_offsets, sorted_pair, pair_pos,

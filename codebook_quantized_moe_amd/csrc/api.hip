@@ -171,6 +171,32 @@ int moeq_permute_by_expert(const int32_t* topk_ids, int T, int k, int E, int32_t
     return check_launch(w);
 }
 
+// tokens up to which moeq_route_permute runs as one workgroup (beyond: the two kernels)
+constexpr int kRoutePermuteOneGroup = 64;
+
+int moeq_route_permute(const float* logits, int T, int E, int k, int gating, int32_t* topk_ids,
+                       float* topk_w, int32_t* expert_offsets, int32_t* sorted_pair,
+                       int32_t* pair_pos, void* stream) {
+    const char* w = "moeq_route_permute";
+    if (int r = check_sizes(w, T, k, E)) return r;
+    if (gating != MOEQ_GATING_SOFTMAX_TOPK && gating != MOEQ_GATING_SIGMOID_TOPK)
+        return fail(MOEQ_EINVAL, "%s: unknown gating %d", w, gating);
+    if (!expert_offsets) return fail(MOEQ_EINVAL, "%s: expert_offsets is NULL", w);
+    if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_pair || !pair_pos))
+        return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    const bool sig = gating == MOEQ_GATING_SIGMOID_TOPK;
+    clear_hip_error();
+    if (T <= kRoutePermuteOneGroup) {
+        launch_route_permute(logits, T, E, k, sig, topk_ids, topk_w, expert_offsets, sorted_pair,
+                             pair_pos, (hipStream_t)stream);
+    } else {
+        launch_route_topk(logits, T, E, k, sig, topk_ids, topk_w, (hipStream_t)stream);
+        launch_permute(topk_ids, T * k, E, expert_offsets, sorted_pair, pair_pos,
+                       (hipStream_t)stream);
+    }
+    return check_launch(w);
+}
+
 static int projection(const char* w, bool gateup, const uint16_t* act, int T, int H, int I, int E,
                       int k, const int32_t* offsets, const int32_t* sorted_pair, const float* topk_w,
                       const uint8_t* codes0, const uint8_t* scales0, const uint8_t* codes1,

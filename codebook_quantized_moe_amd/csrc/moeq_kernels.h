@@ -34,6 +34,9 @@ void launch_route_topk(const float* logits, int T, int E, int k, bool sigmoid, i
                        float* w, hipStream_t stream);
 void launch_permute(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pair,
                     int32_t* pair_pos, hipStream_t stream);
+void launch_route_permute(const float* logits, int T, int E, int k, bool sigmoid, int32_t* ids,
+                          float* w, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                          hipStream_t stream);
 void launch_decode(const SkinnyArgs& a, bool gateup, long tiles, int cus, int shape,
                    hipStream_t stream);
 int decode_tile_rows();

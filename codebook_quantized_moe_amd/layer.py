@@ -12,7 +12,7 @@ import numpy as np
 import torch
 
 from . import (MOEQ_GATING_SOFTMAX_TOPK, moeq_down, moeq_gateup_swiglu, moeq_moe_decode,
-               moeq_moe_decode_workspace_bytes, moeq_permute_by_expert,
+               moeq_moe_decode_workspace_bytes, moeq_permute_by_expert, moeq_route_permute,
                moeq_route_topk, moeq_router_logits, moeq_shared_expert,
                moeq_shared_workspace_bytes, moeq_unpermute_combine,
                moeq_unpermute_combine_shared, moeq_workspace_bytes)
@@ -91,6 +91,12 @@ class MoeLayer:
         moeq_route_topk(logits, self.T, self.E, self.k, self.topk_ids, self.topk_w,
                         gating=self.gating, stream=stream)
 
+    def route_permute(self, logits, stream=None):
+        """route then permute (one launch for few tokens)."""
+        moeq_route_permute(logits, self.T, self.E, self.k, self.topk_ids, self.topk_w,
+                           self.offsets, self.sorted_pair, self.pair_pos, gating=self.gating,
+                           stream=stream)
+
     def permute(self, stream=None):
         moeq_permute_by_expert(self.topk_ids, self.T, self.k, self.E, self.offsets,
                                self.sorted_pair, self.pair_pos, stream=stream)
@@ -139,8 +145,7 @@ class MoeLayer:
         and is added in the combine."""
         if shared is not None:
             stream = self._fork_shared(x, shared, stream)
-        self.route(logits, stream)
-        self.permute(stream)
+        self.route_permute(logits, stream)
         self.gateup(x, w, stream)
         self.down(w, stream)
         if shared is not None:
@@ -166,8 +171,7 @@ class MoeLayer:
         if shared is not None:
             stream = self._fork_shared(x, shared, stream)
         self.router(x, router_w, stream)
-        self.route(self.logits, stream)
-        self.permute(stream)
+        self.route_permute(self.logits, stream)
         self.gateup(x, w, stream)
         self.down(w, stream)
         if shared is not None:

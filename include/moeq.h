@@ -136,6 +136,18 @@ int moeq_permute_by_expert(const int32_t* topk_ids, int T, int k, int E, int32_t
                            int32_t* sorted_pair, int32_t* pair_pos, void* stream);
 
 /*
+ * moeq_route_topk followed by moeq_permute_by_expert, with the same results and the same
+ * arguments (the logits in, the five routing arrays out). Up to 64 tokens it is one launch (one
+ * workgroup routes and then permutes); beyond, it launches the two kernels. Errors: the union
+ * of the two calls' errors. (Few-token decode steps spend a launch less on the front of the
+ * path; the pages' decode kernels favour fewer launches: README of
+ * GLM-5.2-EXL3-TR3v4-3.5bpw-MTP78, "Tuning" / "Why".)
+ */
+int moeq_route_permute(const float* logits, int T, int E, int k, int gating, int32_t* topk_ids,
+                       float* topk_w, int32_t* expert_offsets, int32_t* sorted_pair,
+                       int32_t* pair_pos, void* stream);
+
+/*
  * Fused gate|up projection and SwiGLU ("Round 7" brief, decision 4), with the weights decoded
  * from 4-bit codes as they are streamed (model card, "Codes are indices into the per-layer
  * grid"). For each sorted row r of expert e (pair p = sorted_pair[r], token t = p / k):

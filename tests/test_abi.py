@@ -263,3 +263,12 @@ def test_moe_decode_validation():
     a.update(T=0, x=None, ws=None, ws_bytes=0)
     f(**a)                                                 # T = 0: no-op, OK
     assert _status(mq.moeq_moe_decode_check, None, stream=0) == mq.MOEQ_EINVAL
+
+
+def test_route_permute_validation():
+    f = mq.moeq_route_permute
+    assert _status(f, FAKE, 4, 256, 0, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0) == mq.MOEQ_EINVAL
+    assert _status(f, FAKE, 4, 256, 8, FAKE, FAKE, None, FAKE, FAKE, stream=0) == mq.MOEQ_EINVAL
+    assert _status(f, None, 4, 256, 8, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0) == mq.MOEQ_EINVAL
+    assert _status(f, FAKE, 4, 256, 8, FAKE, FAKE, FAKE, FAKE, FAKE, gating=5,
+                   stream=0) == mq.MOEQ_EINVAL

@@ -739,3 +739,27 @@ def test_moe_decode_single_launch(T, E, H, I, k, gating, monkeypatch):
             expect = oracle.bf16_to_f64(ref["x_next"])[toks]
             rel = np.linalg.norm(got - expect, axis=1) / np.linalg.norm(expect, axis=1)
             assert rel.max() < ROW_REL_TOL, rel.max()
+
+
+@pytest.mark.parametrize("T,E,k,gating", [(1, 17, 1, 0), (8, 256, 8, 0), (64, 256, 8, 1),
+                                          (65, 64, 4, 0), (2048, 256, 8, 1)])
+def test_route_permute_equals_the_two_calls(T, E, k, gating):
+    """One launch up to 64 tokens, two beyond: the same five arrays, bit for bit, as
+    moeq_route_topk then moeq_permute_by_expert, and the oracle's routing."""
+    mq = _mq()
+    logits = dev(synth.make_logits(71, T, E, zipf_s=1.0 if T > 64 else None))
+    def bufs():
+        i32 = dict(dtype=torch.int32, device="cuda")
+        return (torch.empty(T * k, **i32), torch.empty(T * k, dtype=torch.float32, device="cuda"),
+                torch.empty(E + 1, **i32), torch.empty(T * k, **i32), torch.empty(T * k, **i32))
+    a, b = bufs(), bufs()
+    mq.moeq_route_permute(logits, T, E, k, *a, gating=gating)
+    mq.moeq_route_topk(logits, T, E, k, b[0], b[1], gating=gating)
+    mq.moeq_permute_by_expert(b[0], T, k, E, b[2], b[3], b[4])
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(host(x).view(np.uint32), host(y).view(np.uint32))
+    rid, rw = oracle.route_topk(host(logits), k, "sigmoid" if gating else "softmax")
+    np.testing.assert_array_equal(host(a[0]).reshape(T, k), rid)
+    ro, rs, rp = oracle.permute_by_expert(rid, E)
+    np.testing.assert_array_equal(host(a[2]), ro)
+    np.testing.assert_array_equal(host(a[3]), rs)
