@@ -49,12 +49,20 @@ __device__ __forceinline__ PairClass classify(int e, bool live, int E) {
     return c;
 }
 
-// The whole permutation, by one workgroup of NW wavefronts (every thread calls it).
-template <int NW>
-__device__ inline void permute_block(const int32_t* __restrict__ ids, int P, int E,
+// What permute_range does with the pairs [pb0, pe0) (every thread of the workgroup calls it):
+//   kPermFull:  the whole permutation (the range is all pairs); writes expert_offsets;
+//   kPermCount: only the range's per-bucket counts, into counts_out[0..E];
+//   kPermPlace: the range's pairs placed from the first positions offsets[e] + base_in[e] it
+//               has in every bucket (base_in may lie in pair_pos inside the range: it is read
+//               first).
+constexpr int kPermFull = 0, kPermCount = 1, kPermPlace = 2;
+
+template <int NW, int MODE>
+__device__ inline void permute_range(const int32_t* __restrict__ ids, int pb0, int pe0, int E,
                                      int32_t* __restrict__ offsets,
                                      int32_t* __restrict__ sorted_pair,
-                                     int32_t* __restrict__ pair_pos) {
+                                     int32_t* __restrict__ pair_pos,
+                                     int32_t* __restrict__ counts_out, const int32_t* base_in) {
     __shared__ int wcnt[NW][kBuckets];   // counts, then running positions
     __shared__ int base[kBuckets];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -63,10 +71,11 @@ __device__ inline void permute_block(const int32_t* __restrict__ ids, int P, int
     for (int i = tid; i < NW * kBuckets; i += (64 * NW)) (&wcnt[0][0])[i] = 0;
     __syncthreads();
 
-    // this wavefront's span of pairs (a multiple of 64 long, except at the end of P)
-    const int span = ((P + 64 * NW - 1) / (64 * NW)) * 64;
-    const int pb = wave * span;
-    const int pe = min(P, pb + span);
+    // this wavefront's span of the range (a multiple of 64 long, except at the range's end)
+    const int n = pe0 - pb0;
+    const int span = ((n + 64 * NW - 1) / (64 * NW)) * 64;
+    const int pb = pb0 + wave * span;
+    const int pe = min(pe0, pb + span);
 
     // the ids of kBatch groups are loaded before the first of them is classified (one memory
     // round trip per batch instead of one per group)
@@ -100,12 +109,15 @@ __device__ inline void permute_block(const int32_t* __restrict__ ids, int P, int
             wcnt[w][b] = run;
             run += c;
         }
-        base[b] = run;
+        if (MODE == kPermCount) counts_out[b] = run;
+        else if (MODE == kPermPlace) base[b] = offsets[b] + base_in[b];
+        else base[b] = run;
     }
+    if (MODE == kPermCount) return;
     __syncthreads();
 
     // exclusive scan over buckets 0..E (E + 1 <= 257 entries): wave 0, 5 entries per lane
-    if (wave == 0) {
+    if (MODE == kPermFull && wave == 0) {
         int local[5];
         int s = 0;
 #pragma unroll
@@ -144,6 +156,15 @@ __device__ inline void permute_block(const int32_t* __restrict__ ids, int P, int
             if (c.live && rank == 0) wcnt[wave][c.bucket] += __popcll(c.same);
         }
     }
+}
+
+// The whole permutation, by one workgroup of NW wavefronts (every thread calls it).
+template <int NW>
+__device__ inline void permute_block(const int32_t* __restrict__ ids, int P, int E,
+                                     int32_t* __restrict__ offsets,
+                                     int32_t* __restrict__ sorted_pair,
+                                     int32_t* __restrict__ pair_pos) {
+    permute_range<NW, kPermFull>(ids, 0, P, E, offsets, sorted_pair, pair_pos, nullptr, nullptr);
 }
 
 }  // namespace moeq

@@ -286,6 +286,26 @@ def test_permute_invalid_ids_are_placed_last():
     assert host(off)[E] == 4
 
 
+@pytest.mark.parametrize("P,E", [(4096, 256), (4097, 17), (40000, 256), (65536 + 1000, 64)])
+def test_permute_many_pairs_with_invalid_ids(P, E):
+    """The three-launch form (blocks of 1024 pairs, the last one larger), skewed ids and
+    invalid ids scattered through several blocks."""
+    mq = _mq()
+    g = np.random.default_rng(P)
+    ids = np.minimum(g.zipf(1.3, P) - 1, E - 1).astype(np.int32)
+    bad = g.choice(P, 37, replace=False)
+    ids[bad] = g.choice([-1, E, E + 5, 1 << 30, -(1 << 30)], 37)
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(P, dtype=torch.int32, device="cuda")
+    pp = torch.empty(P, dtype=torch.int32, device="cuda")
+    mq.moeq_permute_by_expert(dev(ids), P, 1, E, off, sp, pp)
+    ro, rs, rp = oracle.permute_by_expert(ids.reshape(P, 1), E)
+    np.testing.assert_array_equal(host(off), ro)
+    np.testing.assert_array_equal(host(sp), rs)
+    np.testing.assert_array_equal(host(pp), rp)
+    assert host(off)[E] == P - 37
+
+
 # ----------------------------------------------------------------------------------------------
 # whole layer
 # ----------------------------------------------------------------------------------------------
