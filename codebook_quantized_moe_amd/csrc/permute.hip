@@ -1,5 +1,6 @@
-// Stable counting sort of the (token, slot) pairs by expert: one workgroup of 16 wavefronts
-// running permute_block.
+// Stable counting sort of the (token, slot) pairs by expert (the walks are permute_range):
+// below 4096 pairs one workgroup of 16 wavefronts; from 4096 pairs three launches over blocks
+// of pairs (below); and, for few tokens, routing followed by the permutation in one workgroup.
 #include "permute_device.h"
 #include "route_device.h"
 
