@@ -99,17 +99,37 @@ struct ExpertMeta {
     int n;
 };
 
-// Fills m (all threads call it; ends with a barrier). Returns the count of active experts.
-__device__ inline int active_tiles(const int32_t* offsets, const uint8_t* table_id, int E,
-                                   ExpertMeta& m) {
+// What the first wavefront reads for the expert map: lane l takes experts 4 l .. 4 l + 3.
+// The indexes are clamped into the arrays (offsets has E + 1 entries, E >= 1), so the loads
+// need no branches and go out together; an expert e >= E gets zero rows.
+struct MetaLoads {
+    int beg[4], end[4], tsel[4];
+};
+
+__device__ __forceinline__ MetaLoads load_meta(const int32_t* offsets, const uint8_t* table_id,
+                                               int E) {
+    const int lane = threadIdx.x & 63;
+    MetaLoads l;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane * 4 + j;
+        l.beg[j] = offsets[min(e, E)];
+        l.end[j] = offsets[min(e + 1, E)];
+        l.tsel[j] = table_id[min(e, E - 1)];
+    }
+    return l;
+}
+
+// Fills m from the first wavefront's loads ml (all threads call it; ends with a barrier).
+// Returns the count of active experts.
+__device__ inline int active_tiles(const MetaLoads& ml, ExpertMeta& m) {
     const int lane = threadIdx.x & 63;
     if (threadIdx.x < 64) {
         int rows[4], beg[4], c = 0, nt = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int e = lane * 4 + j;
-            beg[j] = e < E ? offsets[e] : 0;
-            rows[j] = e < E ? offsets[e + 1] - beg[j] : 0;
+            beg[j] = ml.beg[j];
+            rows[j] = ml.end[j] - ml.beg[j];
             c += rows[j] > 0;
             nt += (rows[j] + kTileRows - 1) / kTileRows;
         }
@@ -128,7 +148,7 @@ __device__ inline int active_tiles(const int32_t* offsets, const uint8_t* table_
                 m.tpre[pos] = pre;
                 m.beg[pos] = beg[j];
                 m.cnt[pos] = rows[j];
-                m.tsel[pos] = table_id[e];
+                m.tsel[pos] = ml.tsel[j];
                 ++pos;
                 pre += (rows[j] + kTileRows - 1) / kTileRows;
             }
@@ -178,7 +198,9 @@ __device__ __forceinline__ int weight_row(int cb, int w, int g, int q, int* mat)
 
 // One projection over the whole persistent grid (every workgroup calls it; it returns when
 // the workgroup's items are done). smem: the launch's dynamic LDS; meta: LDS for the item map.
-template <bool GATEUP, class S>
+// SALIGN (only when every weight row's scale bytes start on a 16-byte boundary, K/32 a
+// multiple of 16) stages 16 fewer scale bytes per row; the other form works for any K.
+template <bool GATEUP, class S, bool SALIGN>
 __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, ExpertMeta& meta) {
     constexpr int kChunkK = S::kChunkK, kRowsPerWG = S::kRowsPerWG;
     constexpr int kARowUnits = S::kARowUnits, kABufBytes = S::kABufBytes;
@@ -190,13 +212,19 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
     uint8_t* rowinfo = sbuf + 2 * kSBufBytes;
     uint16_t* row_tok = reinterpret_cast<uint16_t*>(rowinfo);
     float* row_w = reinterpret_cast<float*>(rowinfo);
+    // the prologue's first loads go out before the table build, which hides their latency
+    const int P = a.T * a.k;
+    const bool has_row = (int)threadIdx.x < P;
+    const int p0 = has_row ? a.sorted_pair[threadIdx.x] : 0;
+    MetaLoads ml;
+    if (threadIdx.x < 64) ml = load_meta(a.offsets, a.table_id, a.E);
     build_decode_tables(a.tables, tab);
-    for (int r = threadIdx.x; r < a.T * a.k; r += blockDim.x) {
-        const int p = a.sorted_pair[r];
+    for (int r = threadIdx.x; r < P; r += blockDim.x) {
+        const int p = r == (int)threadIdx.x ? p0 : a.sorted_pair[r];
         if (GATEUP) row_tok[r] = (uint16_t)(p / a.k);
         else row_w[r] = a.topk_w[p];
     }
-    const int nact = active_tiles(a.offsets, a.table_id, a.E, meta);
+    const int nact = active_tiles(ml, meta);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -262,21 +290,25 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
     //     the rows are already in pair-split K order (x is split once per call, the
     //     intermediate is stored that way);
     //   * scales: row R of the item (gate|up: R = 64 mat + channel, so gate rows and up rows
-    //     fill separate DMA loads) gets kSRowBytes bytes from the 16-byte boundary at or
-    //     below its first scale byte of the chunk; readers add the row's offset (row * K/32
-    //     mod 16). Bytes past a row's K are masked at read time.
+    //     fill separate DMA loads) gets kSRow bytes from the 16-byte boundary at or below its
+    //     first scale byte of the chunk; readers add the row's offset (row * K/32 mod 16, zero
+    //     when SALIGN, which needs no extra 16 bytes per row). Bytes past a row's K are masked
+    //     at read time.
     constexpr int kAUnits = kTileRows * kARowUnits;
     constexpr int kALoads = (kAUnits + 63) / 64;
-    constexpr int kSLoads = kSBufBytes / 1024;
-    constexpr int kSUnitsPerRow = kSRowBytes / 16;
-    static_assert(kSBufBytes % 1024 == 0 && (kRowsPerWG / 2) * kSRowBytes % 1024 == 0,
+    constexpr int kSRow = SALIGN ? kChunkK / 32 : kSRowBytes;
+    constexpr int kSLoads = kRowsPerWG * kSRow / 1024;
+    constexpr int kSUnitsPerRow = kSRow / 16;
+    static_assert(kRowsPerWG * kSRow <= kSBufBytes && (kRowsPerWG / 2) * kSRow % 1024 == 0,
                   "scale staging: whole DMA loads, gate and up rows in separate loads");
     auto stage_dma = [&](const Src& sr, int chunk, int sbufi) {
         const int kc = chunk * kChunkK;
         uint8_t* ab = abuf + sbufi * kABufBytes;
         uint8_t* sbb = sbuf + sbufi * kSBufBytes;
-        for (int i = wave; i < kALoads + kSLoads; i += S::kWaves) {
-            if (i < kALoads) {
+        const int na = min(kALoads, (sr.rows * kARowUnits + 63) / 64);
+        const int nall = sr.rows > 0 ? na + kSLoads : 0;
+        for (int i = wave; i < nall; i += S::kWaves) {
+            if (i < na) {
                 const int u = i * 64 + lane;
                 const int row = u / kARowUnits, p = u % kARowUnits;
                 uint32_t off = kOutOfRange;
@@ -288,7 +320,7 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
                 if (u < kAUnits)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(ract, ab + i * 1024, 16, off, 0, 0, 0);
             } else {
-                const int j = i - kALoads;
+                const int j = i - na;
                 const int u = j * 64 + lane;
                 const int R = u / kSUnitsPerRow, piece = u % kSUnitsPerRow;
                 int wrow, mat;
@@ -322,10 +354,10 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
     Src cur = make_src(first);
     Src nxt = make_src(first + stride);
     stage_dma(cur, 0, 0);
-    MOEQ_DEC_WAIT_VMCNT(0);
-    __syncthreads();
     u32x4 cA[4], cB[4];
     load_step(cur, 0, cA);
+    MOEQ_DEC_WAIT_VMCNT(4);        // the staging has landed; the 4 code loads may be in flight
+    __syncthreads();
     int buf = 0;
 
     for (long n = 0; n < nmine; ++n) {
@@ -339,7 +371,7 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
             const int wrow = weight_row<GATEUP, S>(cur.cb, wave, g, q, &mat);
             const int R = GATEUP ? mat * (kRowsPerWG / 2) + (wrow - cur.cb * S::kChannelsPerWG)
                                  : wrow - cur.cb * kRowsPerWG;
-            soff[g] = R * kSRowBytes + (int)(((uint32_t)wrow * ks) & 15u);
+            soff[g] = SALIGN ? R * kSRow : R * kSRow + (int)(((uint32_t)wrow * ks) & 15u);
             acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         auto compute = [&](const u32x4 (&c)[4], int kk) {
@@ -435,13 +467,16 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
     }
 }
 
-template <bool GATEUP, class S>
+template <bool GATEUP, class S, bool SALIGN>
 __global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 decode_kernel(const SkinnyArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ ExpertMeta meta;
-    decode_body<GATEUP, S>(a, smem, meta);
+    decode_body<GATEUP, S, SALIGN>(a, smem, meta);
 }
+
+// scale rows of K/32 bytes all start on a 16-byte boundary
+static bool scale_rows_aligned(const SkinnyArgs& a) { return (a.K / 32) % 16 == 0; }
 
 template <class S>
 static void launch_shape(const SkinnyArgs& a, bool gateup, long items, int cus, hipStream_t stream) {
@@ -449,12 +484,19 @@ static void launch_shape(const SkinnyArgs& a, bool gateup, long items, int cus, 
                        (size_t)a.T * a.k * (gateup ? 2 : 4);
     const int per_cu = 16 / S::kWaves;                    // 4 wavefronts per SIMD
     const long blocks = std::max(1L, std::min(items, (long)cus * per_cu));
-    if (gateup)
-        hipLaunchKernelGGL((decode_kernel<true, S>), dim3(blocks), dim3(S::kThreads), lds,
+    const bool al = scale_rows_aligned(a);
+    if (gateup && al)
+        hipLaunchKernelGGL((decode_kernel<true, S, true>), dim3(blocks), dim3(S::kThreads), lds,
+                           stream, a);
+    else if (gateup)
+        hipLaunchKernelGGL((decode_kernel<true, S, false>), dim3(blocks), dim3(S::kThreads), lds,
+                           stream, a);
+    else if (al)
+        hipLaunchKernelGGL((decode_kernel<false, S, true>), dim3(blocks), dim3(S::kThreads), lds,
                            stream, a);
     else
-        hipLaunchKernelGGL((decode_kernel<false, S>), dim3(blocks), dim3(S::kThreads), lds,
-                           stream, a);
+        hipLaunchKernelGGL((decode_kernel<false, S, false>), dim3(blocks), dim3(S::kThreads),
+                           lds, stream, a);
 }
 
 int decode_tile_rows() { return kTileRows; }
@@ -527,10 +569,10 @@ decode_layer_kernel(const DecodeLayerArgs L) {
     }
     grid_barrier(L.barrier, nwg);
     stamp(1);
-    decode_body<true, S>(L.gu, smem, meta);
+    decode_body<true, S, false>(L.gu, smem, meta);
     grid_barrier(L.barrier, 2 * nwg);
     stamp(2);
-    decode_body<false, S>(L.dn, smem, meta);
+    decode_body<false, S, false>(L.dn, smem, meta);
     grid_barrier(L.barrier, 3 * nwg);
     stamp(3);
     // phase 4: combine, 4 columns per thread

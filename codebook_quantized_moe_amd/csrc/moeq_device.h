@@ -80,7 +80,9 @@ __device__ inline uint32_t scaled_bf16_bits(float t, int s) {
 // of a workgroup; ends with a barrier.
 __device__ inline void build_decode_tables(const TableArgs& ta, u32x4* tab) {
     for (int i = threadIdx.x; i < ta.n * 256; i += blockDim.x) {
-        const int t = i >> 8, s = i & 255;
+        // t is the same in every lane of a wavefront (blockDim is a multiple of 64): as a
+        // scalar, its 8 magnitudes come by one scalar load instead of 8 dependent vector loads
+        const int t = __builtin_amdgcn_readfirstlane(i >> 8), s = i & 255;
         uint32_t h0 = 0, h1 = 0, l0 = 0, l1 = 0;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
