@@ -1,6 +1,7 @@
 // Stable counting sort of the (token, slot) pairs by expert (the walks are permute_range):
-// below 4096 pairs one workgroup of 16 wavefronts; from 4096 pairs three launches over blocks
-// of pairs (below); and, for few tokens, routing followed by the permutation in one workgroup.
+// up to 64 pairs one wavefront (permute_wave); below 4096 pairs one workgroup of 16
+// wavefronts; from 4096 pairs three launches over blocks of pairs (below); and, for few tokens,
+// routing followed by the permutation in one workgroup.
 #include "permute_device.h"
 #include "route_device.h"
 
@@ -16,16 +17,37 @@ __global__ void __launch_bounds__(64 * kPermWaves) permute_kernel(const int32_t*
     permute_block<kPermWaves>(ids, P, E, offsets, sorted_pair, pair_pos);
 }
 
+// P <= 64 pairs: one wavefront
+__global__ void __launch_bounds__(64) permute_wave_kernel(const int32_t* __restrict__ ids, int P,
+                                                          int E, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_pair,
+                                                          int32_t* __restrict__ pair_pos) {
+    const int lane = threadIdx.x;
+    permute_wave(lane < P ? ids[lane] : 0, P, E, offsets, sorted_pair, pair_pos);
+}
+
 // Routing and permutation in one workgroup of 16 wavefronts (few tokens: one launch instead
 // of two): wavefront w routes tokens w, w + 16, ...; then the permutation of their pairs.
 __global__ void __launch_bounds__(64 * kPermWaves) route_permute_kernel(
     const float* __restrict__ logits, int T, int E, int k, int sigmoid, int32_t* __restrict__ ids,
     float* __restrict__ w, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
     int32_t* __restrict__ pair_pos) {
+    const int P = T * k;
+    if (P <= 64) {
+        // the ids stay in LDS for the one-wavefront permutation
+        __shared__ int32_t sid[64];
+        for (int t = threadIdx.x >> 6; t < T; t += kPermWaves)
+            route_token(logits, t, E, k, sigmoid != 0, ids, w, sid);
+        __syncthreads();
+        if (threadIdx.x < 64)
+            permute_wave(threadIdx.x < P ? sid[threadIdx.x] : 0, P, E, offsets, sorted_pair,
+                         pair_pos);
+        return;
+    }
     for (int t = threadIdx.x >> 6; t < T; t += kPermWaves)
         route_token(logits, t, E, k, sigmoid != 0, ids, w);
     __syncthreads();
-    permute_block<kPermWaves>(ids, T * k, E, offsets, sorted_pair, pair_pos);
+    permute_block<kPermWaves>(ids, P, E, offsets, sorted_pair, pair_pos);
 }
 
 void launch_route_permute(const float* logits, int T, int E, int k, bool sigmoid, int32_t* ids,
@@ -116,6 +138,11 @@ __global__ void __launch_bounds__(64 * kPermWaves) permute_place_kernel(
 
 void launch_permute(const int32_t* ids, int P, int E, int32_t* offsets, int32_t* sorted_pair,
                     int32_t* pair_pos, hipStream_t stream) {
+    if (P <= 64) {
+        hipLaunchKernelGGL(permute_wave_kernel, dim3(1), dim3(64), 0, stream, ids, P, E, offsets,
+                           sorted_pair, pair_pos);
+        return;
+    }
     if (P < 4 * kPermChunk) {
         hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(64 * kPermWaves), 0, stream, ids, P, E,
                            offsets, sorted_pair, pair_pos);

@@ -158,6 +158,51 @@ __device__ inline void permute_range(const int32_t* __restrict__ ids, int pb0, i
     }
 }
 
+// The whole permutation of P <= 64 pairs by one wavefront (all its lanes call it; lane p
+// holds the expert id e of pair p, any value for p >= P). A pair's position is the number of
+// pairs in lower buckets plus the number of earlier pairs in its own bucket; both sets come
+// from the 9 ballots of the bucket bits, taken from the most significant bit down (a lane that
+// differs from this one first at bit j is in a lower bucket when its bit j is 0). The buckets
+// in sorted order go to LDS, and expert_offsets[x] (x = 0..E) is the count of them below x, a
+// lower-bound search. No barrier: the wavefront's LDS operations complete in order.
+__device__ inline void permute_wave(int e, int P, int E, int32_t* __restrict__ offsets,
+                                    int32_t* __restrict__ sorted_pair,
+                                    int32_t* __restrict__ pair_pos) {
+    __shared__ int sb[64];
+    const int lane = threadIdx.x & 63;
+    const bool live = lane < P;
+    const int bucket = (e >= 0 && e < E) ? e : E;
+    uint64_t eq = __ballot(live), lt = 0;
+#pragma unroll
+    for (int bit = 8; bit >= 0; --bit) {
+        const bool one = (bucket >> bit) & 1;
+        const uint64_t m = __ballot(live && one);
+        if (one) {
+            lt |= eq & ~m;
+            eq &= m;
+        } else {
+            eq &= ~m;
+        }
+    }
+    const int pos = __popcll(lt) + __popcll(eq & ((1ull << lane) - 1ull));
+    if (live) {
+        sorted_pair[pos] = lane;
+        pair_pos[lane] = pos;
+        sb[pos] = bucket;
+    }
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        const int x = lane + 64 * j;
+        if (x <= E) {
+            int lo = 0;
+#pragma unroll
+            for (int step = 64; step >= 1; step >>= 1)
+                if (lo + step <= P && sb[lo + step - 1] < x) lo += step;
+            offsets[x] = lo;
+        }
+    }
+}
+
 // The whole permutation, by one workgroup of NW wavefronts (every thread calls it).
 template <int NW>
 __device__ inline void permute_block(const int32_t* __restrict__ ids, int P, int E,

@@ -53,10 +53,11 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
     return v;
 }
 
-// Route token t (the whole wavefront calls it): ids[t*k + j], w[t*k + j] for j < k.
+// Route token t (the whole wavefront calls it): ids[t*k + j], w[t*k + j] for j < k; the ids
+// also into lds_ids[t*k + j] when it is given.
 __device__ inline void route_token(const float* __restrict__ logits, int t, int E, int k,
                                    bool sigmoid, int32_t* __restrict__ ids,
-                                   float* __restrict__ w) {
+                                   float* __restrict__ w, int32_t* lds_ids = nullptr) {
     const int lane = threadIdx.x & 63;
     const float* row = logits + (size_t)t * E;
     uint64_t key[4];
@@ -115,6 +116,7 @@ __device__ inline void route_token(const float* __restrict__ logits, int t, int 
         if (slot < k) {
             ids[(size_t)t * k + slot] = my_id[j];
             w[(size_t)t * k + slot] = ex[j] / sum;
+            if (lds_ids) lds_ids[t * k + slot] = my_id[j];
         }
     }
 }

@@ -257,8 +257,10 @@ def test_layer_routed_sigmoid(path):
 
 
 @pytest.mark.parametrize("T,k,E", [(16, 2, 4), (8, 8, 256), (2048, 8, 256), (8192, 8, 256),
-                                   (1, 1, 1), (129, 3, 7)])
+                                   (1, 1, 1), (129, 3, 7), (21, 3, 5), (13, 5, 256)])
 def test_permute_bitexact(T, k, E):
+    """Up to 64 pairs one wavefront (1, 32, 63, 64 pairs here), then one workgroup (65, 387),
+    then three launches."""
     mq = _mq()
     ids = np.random.default_rng(T * 31 + E).integers(0, E, T * k).astype(np.int32)
     off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
@@ -284,6 +286,24 @@ def test_permute_invalid_ids_are_placed_last():
     np.testing.assert_array_equal(host(sp), rs)
     np.testing.assert_array_equal(host(pp), rp)
     assert host(off)[E] == 4
+
+
+@pytest.mark.parametrize("P,E", [(64, 256), (64, 3), (65, 256)])
+def test_permute_invalid_ids_small(P, E):
+    """Invalid ids (negative and >= E) mixed with repeated valid ones, at the largest size of the
+    one-wavefront form and one pair beyond it."""
+    mq = _mq()
+    g = np.random.default_rng(P * 7 + E)
+    ids = g.integers(-2, E + 2, P).astype(np.int32)
+    ids[::9] = E + 1000
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(P, dtype=torch.int32, device="cuda")
+    pp = torch.empty(P, dtype=torch.int32, device="cuda")
+    mq.moeq_permute_by_expert(dev(ids), P, 1, E, off, sp, pp)
+    ro, rs, rp = oracle.permute_by_expert(ids.reshape(P, 1), E)
+    np.testing.assert_array_equal(host(off), ro)
+    np.testing.assert_array_equal(host(sp), rs)
+    np.testing.assert_array_equal(host(pp), rp)
 
 
 @pytest.mark.parametrize("P,E", [(4096, 256), (4097, 17), (40000, 256), (65536 + 1000, 64)])
@@ -761,8 +781,8 @@ def test_moe_decode_single_launch(T, E, H, I, k, gating, monkeypatch):
             assert rel.max() < ROW_REL_TOL, rel.max()
 
 
-@pytest.mark.parametrize("T,E,k,gating", [(1, 17, 1, 0), (8, 256, 8, 0), (64, 256, 8, 1),
-                                          (65, 64, 4, 0), (2048, 256, 8, 1)])
+@pytest.mark.parametrize("T,E,k,gating", [(1, 17, 1, 0), (8, 256, 8, 0), (7, 40, 9, 1),
+                                          (64, 256, 8, 1), (65, 64, 4, 0), (2048, 256, 8, 1)])
 def test_route_permute_equals_the_two_calls(T, E, k, gating):
     """One launch up to 64 tokens, two beyond: the same five arrays, bit for bit, as
     moeq_route_topk then moeq_permute_by_expert, and the oracle's routing."""
