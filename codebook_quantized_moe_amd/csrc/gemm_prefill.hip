@@ -76,8 +76,10 @@ __device__ inline int p_active_tiles(const int32_t* offsets, int E, int* active,
         int rows[4], c = 0, nt = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            // clamped indexes (offsets has E + 1 entries): no branches between the loads, and
+            // an expert e >= E gets no rows
             const int e = lane * 4 + j;
-            rows[j] = e < E ? (offsets[e + 1] - offsets[e] + kPBM - 1) / kPBM : 0;
+            rows[j] = (offsets[min(e + 1, E)] - offsets[min(e, E)] + kPBM - 1) / kPBM;
             c += rows[j] > 0;
             nt += rows[j];
         }
