@@ -305,7 +305,11 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
         const int kc = chunk * kChunkK;
         uint8_t* ab = abuf + sbufi * kABufBytes;
         uint8_t* sbb = sbuf + sbufi * kSBufBytes;
-        const int na = min(kALoads, (sr.rows * kARowUnits + 63) / 64);
+        // Activation loads whose units all lie past the item's last real unit (the rows past
+        // its row count, and that row's padding unit) are not issued: those rows only reach
+        // outputs that are never written. An item past the end issues nothing.
+        const int na =
+            min(kALoads, ((sr.rows - 1) * kARowUnits + kChunkK / 8 + 63) / 64);
         const int nall = sr.rows > 0 ? na + kSLoads : 0;
         for (int i = wave; i < nall; i += S::kWaves) {
             if (i < na) {
