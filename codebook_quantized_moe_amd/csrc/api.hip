@@ -208,6 +208,9 @@ static int projection(const char* w, bool gateup, const uint16_t* act, int T, in
     SkinnyArgs a;
     memset(&a, 0, sizeof(a));
     if (int r = check_tables(w, tables, n_tables, &a.tables)) return r;
+    // no tokens: nothing is read or written, so the arrays may be NULL (an empty tensor's
+    // address), as for routing, permutation and combine
+    if (T == 0 && launch) return ok();
     if (!act || !offsets || !sorted_pair || !codes0 || !scales0 || !table_id || !out ||
         (gateup && (!codes1 || !scales1)) || (!gateup && !topk_w))
         return fail(MOEQ_EINVAL, "%s: null pointer", w);

@@ -165,6 +165,7 @@ int moeq_route_permute(const float* logits, int T, int E, int k, int gating, int
  *            only rows < expert_offsets[E] are written. It is the library's layout for the
  *            intermediate, read back by moeq_down.
  *   ws       device workspace of at least moeq_workspace_bytes(T, k, E, H, I) bytes
+ * T = 0 is a no-op once the sizes and tables pass (the arrays may then be NULL).
  * Errors: MOEQ_EINVAL (null pointer, sizes, table values), MOEQ_EUNSUPPORTED (H or I not a
  * multiple of 64, misalignment), MOEQ_EWORKSPACE.
  */
@@ -184,7 +185,7 @@ int moeq_gateup_swiglu(const uint16_t* x, int T, int H, int I, int E, int k,
  *   topk_w fp32 [T*k] from moeq_route_topk
  *   down codes uint8 [E, H, I/2], scales uint8 [E, H, I/32]
  *   yp     fp32 [T*k, H] out; rows >= expert_offsets[E] are not written
- * Tables, table_id, ws and errors as for moeq_gateup_swiglu.
+ * Tables, table_id, ws, T = 0 and errors as for moeq_gateup_swiglu.
  */
 int moeq_down(const uint16_t* inter, int T, int H, int I, int E, int k,
               const int32_t* expert_offsets, const int32_t* sorted_pair, const float* topk_w,

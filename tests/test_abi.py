@@ -116,6 +116,22 @@ def test_gateup_validation():
         assert _status(mq.moeq_gateup_swiglu, **_gateup(**over)) == code, over
 
 
+def test_projections_accept_no_tokens():
+    """T = 0 is a no-op with NULL per-token arrays (an empty tensor's address is NULL), as for
+    routing, permutation and combine; sizes and tables are still checked first."""
+    none = dict(x=None, T=0, expert_offsets=None, sorted_pair=None, inter=None)
+    mq.moeq_gateup_swiglu(**_gateup(**none))
+    assert mq.moeq_last_error() == ""
+    mq.moeq_down(None, 0, 6144, 2048, 256, 8, None, None, None, FAKE, FAKE, GOOD_TABLES, FAKE,
+                 None, stream=0)
+    assert mq.moeq_last_error() == ""
+    assert _status(mq.moeq_gateup_swiglu, **_gateup(H=6000, **none)) == mq.MOEQ_EUNSUPPORTED
+    assert _status(mq.moeq_gateup_swiglu,
+                   **_gateup(tables=np.array([[np.nan] * 8], np.float32), **none)) == mq.MOEQ_EINVAL
+    assert _status(mq.moeq_down, None, -1, 6144, 2048, 256, 8, None, None, None, FAKE, FAKE,
+                   GOOD_TABLES, FAKE, None, stream=0) == mq.MOEQ_EINVAL
+
+
 def test_down_and_combine_validation():
     assert _status(mq.moeq_down, FAKE, 8, 6144, 2048, 256, 8, FAKE, FAKE, None, FAKE, FAKE,
                    GOOD_TABLES, FAKE, FAKE, stream=0) == mq.MOEQ_EINVAL       # topk_w NULL

@@ -345,6 +345,27 @@ def test_layer_tiny_config(path):
     check_layer(out, ref, c.k)
 
 
+def test_layer_empty_batch(path):
+    """No tokens: the routing front end still writes expert_offsets (all zero), every other
+    call is a no-op on empty (NULL-address) tensors, and the output is empty."""
+    mq = _mq()
+    c = synth.CONFIGS[1]
+    lw, _, _ = _case(1, c.T, c.E, c.H, c.I, c.k)
+    w = mq.DeviceWeights.from_host(lw)
+    L = mq.MoeLayer(0, c.H, c.I, c.E, c.k)
+    L.offsets.fill_(-7)
+    x = torch.empty((0, c.H), dtype=torch.int16, device="cuda")
+    lg = torch.empty((0, c.E), dtype=torch.float32, device="cuda")
+    y = L.forward(x, lg, w, residual=x, out=x)
+    assert tuple(y.shape) == (0, c.H)
+    np.testing.assert_array_equal(host(L.offsets), np.zeros(c.E + 1, np.int32))
+    L.offsets.fill_(-7)
+    L.permute()
+    np.testing.assert_array_equal(host(L.offsets), np.zeros(c.E + 1, np.int32))
+    assert tuple(L.forward_fused(x, lg, w).shape) == (0, c.H)
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("T,E,H,I,k", [(37, 8, 576, 320, 4),     # >16 rows per expert, K tails
                                        (1, 16, 256, 128, 16),     # k = E, one token
                                        (64, 4, 256, 192, 4)])     # k = E, 64 rows per expert
