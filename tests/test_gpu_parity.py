@@ -367,6 +367,7 @@ def test_layer_empty_batch(path):
 
 
 @pytest.mark.parametrize("T,E,H,I,k", [(37, 8, 576, 320, 4),     # >16 rows per expert, K tails
+                                       (37, 16, 1024, 512, 4),    # 16-byte aligned scale rows
                                        (1, 16, 256, 128, 16),     # k = E, one token
                                        (64, 4, 256, 192, 4)])     # k = E, 64 rows per expert
 def test_layer_ragged_shapes(T, E, H, I, k, path):
