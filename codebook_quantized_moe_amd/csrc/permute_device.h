@@ -190,6 +190,9 @@ __device__ inline void permute_wave(int e, int P, int E, int32_t* __restrict__ o
         pair_pos[lane] = pos;
         sb[pos] = bucket;
     }
+    // lanes read buckets other lanes wrote: one wavefront, whose LDS accesses complete in
+    // order; the barrier keeps the compiler from moving the reads above the writes
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
         const int x = lane + 64 * j;
