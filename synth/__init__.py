@@ -349,6 +349,9 @@ CONFIGS = {
               zipf_s=1.0, e2m1=E2M1_DEFECT_EXPERTS, permute="random"),
 }
 
+# the same workloads by name (the numeric ids above also seed their inputs)
+WORKLOADS = {c.name: c for c in CONFIGS.values()}
+
 
 def expected_touched(E: int, k: int, T: int) -> float:
     return E * (1.0 - (1.0 - k / E) ** T)

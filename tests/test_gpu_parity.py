@@ -338,7 +338,7 @@ def _case(cfg_id, T, E, H, I, k, **kw):
 
 
 def test_layer_tiny_config(path):
-    c = synth.CONFIGS[1]
+    c = synth.WORKLOADS["tiny"]
     lw, x, logits = _case(1, c.T, c.E, c.H, c.I, c.k)
     out = run_layer(lw, x, logits, c.k)
     ref = oracle.layer_forward(x, logits, c.k, lw)
@@ -349,7 +349,7 @@ def test_layer_empty_batch(path):
     """No tokens: the routing front end still writes expert_offsets (all zero), every other
     call is a no-op on empty (NULL-address) tensors, and the output is empty."""
     mq = _mq()
-    c = synth.CONFIGS[1]
+    c = synth.WORKLOADS["tiny"]
     lw, _, _ = _case(1, c.T, c.E, c.H, c.I, c.k)
     w = mq.DeviceWeights.from_host(lw)
     L = mq.MoeLayer(0, c.H, c.I, c.E, c.k)
@@ -454,12 +454,12 @@ def test_layer_deterministic(path):
 
 @pytest.fixture(scope="module")
 def glm_layer():
-    c = synth.CONFIGS[2]
+    c = synth.WORKLOADS["glm_decode_t8"]
     return synth.make_layer(2, c.E, c.H, c.I)
 
 
 def test_glm_decode_t8_full(glm_layer):
-    c = synth.CONFIGS[2]
+    c = synth.WORKLOADS["glm_decode_t8"]
     x = synth.make_x(2, c.T, c.H)
     logits = synth.make_logits(2, c.T, c.E)
     out = run_layer(glm_layer, x, logits, c.k)
@@ -480,7 +480,7 @@ def _sample_tokens(ids, n, seed):
 
 
 def test_glm_prefill_t2048_zipf_sampled():
-    c = synth.CONFIGS[3]
+    c = synth.WORKLOADS["glm_prefill_t2048_zipf"]
     lw = synth.make_layer(3, c.E, c.H, c.I)
     x = synth.make_x(3, c.T, c.H)
     logits = synth.make_logits(3, c.T, c.E, zipf_s=c.zipf_s)
@@ -493,7 +493,7 @@ def test_glm_prefill_t2048_zipf_sampled():
 def test_glm_prefill_t8192_e2m1_permuted_sampled():
     """8192 tokens, Zipf routing, the E2M1 experts of the model card's defect table and a
     random intermediate-channel permutation baked into gate-N, up-N and down-K."""
-    c = synth.CONFIGS[5]
+    c = synth.WORKLOADS["glm_prefill_t8192_zipf_e2m1_perm"]
     lw = synth.make_layer(5, c.E, c.H, c.I, e2m1_experts=c.e2m1, permute=c.permute)
     x = synth.make_x(5, c.T, c.H)
     logits = synth.make_logits(5, c.T, c.E, zipf_s=c.zipf_s)
@@ -601,7 +601,7 @@ def test_layer_with_shared_expert(T, E, H, I, k, path):
 
 def test_glm_decode_t8_with_shared_expert(glm_layer):
     mq = _mq()
-    c = synth.CONFIGS[2]
+    c = synth.WORKLOADS["glm_decode_t8"]
     x = synth.make_x(2, c.T, c.H)
     logits = synth.make_logits(2, c.T, c.E)
     sw = synth.make_shared(2, c.H, c.I)

@@ -62,7 +62,7 @@ class _Stack:
     def __init__(self):
         import codebook_quantized_moe_amd as mq
         self.mq = mq
-        self.c = c = synth.CONFIGS[4]
+        self.c = c = synth.WORKLOADS["glm_stack32_decode_t64"]
         self.ml = mq.MoeLayer(c.T, c.H, c.I, c.E, c.k)
         self.X = torch.from_numpy(synth.make_x(4, c.T, c.H).view(np.int16)).cuda()
         self.layer = 0

@@ -302,7 +302,7 @@ def _dense(lw, perm_back=False):
 
 @pytest.fixture(scope="module")
 def tiny():
-    c = synth.CONFIGS[1]
+    c = synth.WORKLOADS["tiny"]
     lw = synth.make_layer(1, c.E, c.H, c.I)
     x = synth.make_x(1, c.T, c.H)
     logits = synth.make_logits(1, c.T, c.E)
