@@ -121,15 +121,21 @@ __global__ void __launch_bounds__(256) pair_split_rows_kernel(const u32x4* __res
 #define MOEQ_WAIT_VMCNT(n) \
     __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
-// Workgroup barrier without a memory fence. __syncthreads() also makes the compiler wait for
-// every LDS-DMA load in flight, including the ones issued for stages ahead; the stage loop
-// instead waits for the one it needs with MOEQ_WAIT_VMCNT and relies on this barrier for the
-// rest: each wavefront consumes (waits for) every LDS read of a buffer before the barrier
-// after which that buffer is refilled. The empty asm statements keep the compiler from moving
-// memory accesses across the barrier.
+// Workgroup barrier that waits for the wavefront's own LDS reads but not for its vector-memory
+// loads. __syncthreads() also makes the compiler wait for every LDS-DMA load in flight,
+// including the ones issued for stages ahead; the stage loop instead waits for the one it
+// needs with MOEQ_WAIT_VMCNT. The LDS reads issued in kq-step 2 of a stage (the activation
+// fragments of kq-step 3 from the stage's own tile, the next stage's code bytes from a weight
+// tile that the loads after the barrier may refill) are only consumed in kq-step 3, after the
+// barrier; s_barrier does not wait for them, so lgkmcnt(0) comes first: once a wavefront is
+// past the barrier, every LDS read of every wavefront issued before it has returned its data,
+// and the LDS-DMA refills issued after it cannot overwrite a tile under a pending read. The
+// empty asm statements keep the compiler from moving memory accesses across the barrier.
+#define MOEQ_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14))
 #define MOEQ_STAGE_BARRIER()                 \
     do {                                     \
         asm volatile("" ::: "memory");       \
+        MOEQ_WAIT_LGKM0();                   \
         __builtin_amdgcn_s_barrier();        \
         asm volatile("" ::: "memory");       \
     } while (0)
