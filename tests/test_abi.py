@@ -1,42 +1,22 @@
-"""The C-ABI library loads, exports every symbol include/moeq.h declares, and rejects bad
-arguments before launching anything (so these run without a GPU)."""
-import ctypes
-import os
-import re
+"""The C-ABI calls reject bad arguments before launching anything.
 
+These pass a fake device address (FAKE) to calls that must fail in their host-side checks, so
+they run only where no GPU is visible: on a machine with a GPU a regression in those checks
+would launch kernels on that address.
+"""
 import numpy as np
 import pytest
+import torch
 
 import codebook_quantized_moe_amd as mq
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moeq.h")
+pytestmark = pytest.mark.skipif(
+    torch.cuda.is_available(),
+    reason="fake device addresses: host-side validation is tested only where no GPU is visible")
 
 GOOD_TABLES = np.array([[0.13, 0.39, 0.66, 0.94, 1.26, 1.62, 2.07, 2.73],
                         [0, .5, 1, 1.5, 2, 3, 4, 6]], np.float32)
 FAKE = 4096   # a non-null, 16-byte aligned address; never dereferenced by a failing call
-
-
-def _declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = set(re.findall(r"\b(moeq_[a-z_]+)\s*\(", src))
-    names.discard("moeq_inter_slot")           # static inline helper in the header
-    return sorted(names)
-
-
-def test_header_symbols_exported():
-    names = _declared()
-    assert set(names) == set(mq.EXPORTED)
-    lib = ctypes.CDLL(mq.LIB_PATH)
-    for n in names:
-        assert hasattr(lib, n), n
-
-
-def test_inter_slot_matches_header_rule():
-    c = np.arange(64)
-    s = mq.inter_slot(c)
-    assert sorted(s) == list(range(64))
-    np.testing.assert_array_equal(s[:8], [0, 4, 1, 5, 2, 6, 3, 7])
 
 
 def _status(fn, *args, **kw):
