@@ -52,11 +52,13 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for s in SOURCES:
-        obj = os.path.join(objdir, s.replace(".hip", ".o"))
-        _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", obj], verbose)
-        objs.append(obj)
+    from concurrent.futures import ThreadPoolExecutor
+    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
+    # one hipcc per source, a few at a time (each is a separate process)
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1, 8)) as ex:
+        for f in [ex.submit(_run, [HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o], verbose)
+                  for s, o in zip(SOURCES, objs)]:
+            f.result()
     rt = hip_runtime_dir()
     tmp = LIB + ".tmp"
     # plain host link (no implicit -lamdhip64): the device code objects are embedded in the
