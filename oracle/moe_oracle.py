@@ -59,7 +59,8 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "rne_bf16", "total_order_key", "router_logits", "route_topk",
     "permute_by_expert",
-    "unpack_codes", "dequant_bf16", "layer_forward", "shared_expert_forward", "stack_forward",
+    "unpack_codes", "dequant_bf16", "layer_forward", "expert_inter", "shared_expert_forward",
+    "stack_forward",
     "block_scale_bytes", "rtn_encode", "reconstruction_sq_error", "lloyd_stats",
     "lloyd_update", "fit_grid", "select_arms", "E2M1_TABLE",
 ]
@@ -376,6 +377,25 @@ def _silu(g):
     return g / (1.0 + np.exp(-g))
 
 
+def _swiglu_rows(xs, lw, e):
+    """silu(Wg_e x) * (Wu_e x) in fp64 for the activation rows xs [R, H] (fp64 values of bf16
+    activations), [brief] decision 4."""
+    tab = lw.tables[int(lw.table_id[e])]
+    wg = _expert_dense(lw.gate_codes[e], lw.gate_scales[e], tab)
+    g = xs @ wg.T
+    del wg
+    wu = _expert_dense(lw.up_codes[e], lw.up_scales[e], tab)
+    u = xs @ wu.T
+    return _silu(g) * u
+
+
+def expert_inter(x_bits, lw, e, tokens) -> np.ndarray:
+    """The intermediate rows of expert e for the given tokens, as layer_forward forms them:
+    bf16 bits [len(tokens), I] of silu(Wg_e x_t) * (Wu_e x_t), one RNE rounding of the fp64
+    value. Checks every row of one (hot) expert without the other experts' work."""
+    return rne_bf16(_swiglu_rows(bf16_to_f64(np.asarray(x_bits)[np.asarray(tokens)]), lw, e))
+
+
 def shared_expert_forward(x_bits, sw, round_inter=True):
     """The shared expert on every token, in fp64 ([readme] "Checkpoint layout update ...: BF16
     shared experts, merged online K6": one gate/up/down MLP per layer beside the routed ones).
@@ -442,13 +462,7 @@ def layer_forward(x_bits, logits, k, lw, residual_bits=None, tokens=None, round_
             continue
         rows, pairs, tok, slot = rows[keep], pairs[keep], tok[keep], slot[keep]
         tab = lw.tables[int(lw.table_id[e])]
-        wg = _expert_dense(lw.gate_codes[e], lw.gate_scales[e], tab)
-        wu = _expert_dense(lw.up_codes[e], lw.up_scales[e], tab)
-        xs = x[tok]
-        g = xs @ wg.T
-        u = xs @ wu.T
-        del wg, wu
-        a = _silu(g) * u
+        a = _swiglu_rows(x[tok], lw, e)
         if round_inter:
             ib = rne_bf16(a)
             inter[rows] = ib

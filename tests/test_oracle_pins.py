@@ -418,6 +418,64 @@ def test_stack_residual_rounding(tiny):
     np.testing.assert_array_equal(two, step["x_next"])
 
 
+def _plain_bf16(v):
+    """fp64 values -> the nearest bf16 values, ties to even (normal range): 8 significant bits,
+    written from the format (frexp gives v = m 2^e with 1/2 <= |m| < 1)."""
+    m, e = np.frexp(np.asarray(v, dtype=np.float64))
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def _plain_decode(codes, scales, table):
+    """[card] "Contents" / "Codes are indices into the per-layer grid", element by element:
+    code c of byte k // 2 (low nibble for even k), w = (-1)^(bit 3) table[c & 7] 2^(s - 127)
+    with s the scale byte of k // 32, rounded once to bf16."""
+    N, half = codes.shape
+    out = np.empty((N, 2 * half))
+    for kk in range(2 * half):
+        b = codes[:, kk // 2].astype(np.int64)
+        c = (b >> 4) if kk % 2 else (b & 15)
+        mag = np.asarray(table, np.float32).astype(np.float64)[c & 7]
+        out[:, kk] = np.where(c & 8, -1.0, 1.0) * mag * 2.0 ** (scales[:, kk // 32].astype(np.int64) - 127)
+    return _plain_bf16(out)
+
+
+def test_stack_two_distinct_layers_against_a_plain_loop():
+    """Two layers with their own grid, weights, logits and E2M1 expert, X carried in bf16:
+    the oracle's free-running stack against a loop written from the definitions (full sort
+    for the top-k, softmax over the k, element-wise decode, SwiGLU, gate-weighted sum,
+    X + y rounded to bf16 once). Weights N(0, 0.2), so that y is comparable to X and
+    swapping the two layers changes most of the result."""
+    T, H, I, E, k = 6, 128, 64, 5, 2
+    layers = [(synth.make_logits(71, T, E, layer=l),
+               synth.make_layer(71, E, H, I, layer=l, e2m1_experts=(l,), sigma=0.2))
+              for l in range(2)]
+    assert not np.array_equal(layers[0][1].tables[0], layers[1][1].tables[0])
+    x0 = synth.make_x(71, T, H)
+    got = oracle.bf16_to_f64(oracle.stack_forward(x0, layers, k))
+    X = (x0.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for logits, lw in layers:
+        Y = np.zeros((T, H))
+        for t in range(T):
+            order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
+            lg = np.array([float(logits[t, e]) for e in order])
+            p = np.exp(lg - lg.max())
+            p /= p.sum()
+            for j, e in enumerate(order):
+                tab = lw.tables[int(lw.table_id[e])]
+                wg = _plain_decode(lw.gate_codes[e], lw.gate_scales[e], tab)
+                wu = _plain_decode(lw.up_codes[e], lw.up_scales[e], tab)
+                wd = _plain_decode(lw.down_codes[e], lw.down_scales[e], tab)
+                g, u = wg @ X[t], wu @ X[t]
+                a = _plain_bf16(g / (1.0 + np.exp(-g)) * u)
+                Y[t] += p[j] * (wd @ a)
+        X = _plain_bf16(X + Y)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(X))[1] - 8)
+    assert np.all(np.abs(got - X) <= ulp)
+    assert np.mean(got == X) >= 0.99
+    swapped = oracle.bf16_to_f64(oracle.stack_forward(x0, layers[::-1], k))
+    assert np.mean(swapped == got) < 0.5
+
+
 # ----------------------------------------------------------------------------------------------
 # shared expert
 # ----------------------------------------------------------------------------------------------
