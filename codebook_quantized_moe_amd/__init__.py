@@ -34,7 +34,8 @@ EXPORTED = ("moeq_last_error", "moeq_workspace_bytes", "moeq_router_logits", "mo
             "moeq_permute_by_expert", "moeq_route_permute", "moeq_gateup_swiglu", "moeq_down",
             "moeq_unpermute_combine", "moeq_shared_workspace_bytes", "moeq_shared_expert",
             "moeq_unpermute_combine_shared", "moeq_quantize", "moeq_lloyd_workspace_bytes",
-            "moeq_lloyd_stats", "moeq_select_arms", "moeq_moe_decode_workspace_bytes",
+            "moeq_lloyd_stats", "moeq_lloyd_update", "moeq_select_arms",
+            "moeq_moe_decode_workspace_bytes",
             "moeq_moe_decode", "moeq_moe_decode_check", "moeq_debug_dequant")
 
 _i, _vp, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
@@ -72,6 +73,8 @@ _lib.moeq_lloyd_workspace_bytes.restype = _sz
 _lib.moeq_lloyd_workspace_bytes.argtypes = [_i, _i]
 _lib.moeq_lloyd_stats.restype = _i
 _lib.moeq_lloyd_stats.argtypes = [_vp, _i, _i, _i, _vp, _f, _i, _vp, _vp, _sz, _vp]
+_lib.moeq_lloyd_update.restype = _i
+_lib.moeq_lloyd_update.argtypes = [_vp, _vp, _vp, _vp]
 _lib.moeq_select_arms.restype = _i
 _lib.moeq_select_arms.argtypes = [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]
 _lib.moeq_moe_decode_workspace_bytes.restype = _sz
@@ -212,6 +215,18 @@ def moeq_lloyd_stats(w, E, N, K, table, gmax, accumulate, stats, ws, ws_bytes, s
     _check(_lib.moeq_lloyd_stats(_p(w), E, N, K, tab.ctypes.data, float(gmax),
                                  1 if accumulate else 0, _p(stats), _p(ws), ws_bytes,
                                  _stream(stream)))
+
+
+def moeq_lloyd_update(stats, table):
+    """stats: host float64 [24] from moeq_lloyd_stats; table: the 8 magnitudes they were taken
+    against. Returns (next fp32 table [8], weighted squared error of the assignment)."""
+    st = np.ascontiguousarray(np.asarray(stats, dtype=np.float64).reshape(24))
+    tab = np.ascontiguousarray(np.asarray(table, dtype=np.float32).reshape(8))
+    nxt = np.empty(8, np.float32)
+    err = ctypes.c_double(0.0)
+    _check(_lib.moeq_lloyd_update(st.ctypes.data, tab.ctypes.data, nxt.ctypes.data,
+                                  ctypes.addressof(err)))
+    return nxt, err.value
 
 
 def moeq_select_arms(err_a, err_b, E, N, accumulate, table_id, expert_err, stream=None):

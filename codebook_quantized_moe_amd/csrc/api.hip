@@ -451,6 +451,20 @@ int moeq_lloyd_stats(const uint16_t* wts, int E, int N, int K, const float* tabl
     return check_launch(w);
 }
 
+int moeq_lloyd_update(const double* stats, const float* table, float* next, double* sq_error) {
+    const char* w = "moeq_lloyd_update";
+    if (!stats || !table || !next) return fail(MOEQ_EINVAL, "%s: null pointer", w);
+    float out[8];
+    double err = 0.0;
+    for (int m = 0; m < 8; ++m) {
+        out[m] = stats[8 + m] > 0.0 ? (float)(stats[m] / stats[8 + m]) : table[m];
+        err += stats[16 + m];
+    }
+    for (int m = 0; m < 8; ++m) next[m] = out[m];
+    if (sq_error) *sq_error = err;
+    return ok();
+}
+
 int moeq_select_arms(const double* err_a, const double* err_b, int E, int N, int accumulate,
                      uint8_t* table_id, double* expert_err, void* stream) {
     const char* w = "moeq_select_arms";

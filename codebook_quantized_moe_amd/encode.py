@@ -2,15 +2,16 @@
 
 Plumbing only: torch holds the device buffers; every pass over the weights is a libmoeq
 kernel (moeq_lloyd_stats, moeq_quantize, moeq_select_arms). The host reads back the 24 sums
-of each grid-fit round and forms the next 8 magnitudes (the tables travel to the kernels as
-host arrays).
+of each grid-fit round and moeq_lloyd_update forms the next 8 magnitudes from them (the
+tables travel to the kernels as host arrays).
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-from . import (moeq_lloyd_stats, moeq_lloyd_workspace_bytes, moeq_quantize, moeq_select_arms)
+from . import (moeq_lloyd_stats, moeq_lloyd_update, moeq_lloyd_workspace_bytes, moeq_quantize,
+               moeq_select_arms)
 
 E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float32)
 
@@ -30,10 +31,8 @@ def fit_grid(mats, table0, iters: int, stream=None):
         for i, m in enumerate(mats):
             E, N, K = m.shape
             moeq_lloyd_stats(m, E, N, K, tab, g0, i > 0, stats, ws, need, stream=stream)
-        st = stats.cpu().numpy().reshape(3, 8)
-        dist.append(float(st[2].sum()))
-        tab = np.where(st[1] > 0, st[0] / np.where(st[1] > 0, st[1], 1.0),
-                       tab.astype(np.float64)).astype(np.float32)
+        tab, err = moeq_lloyd_update(stats.cpu().numpy(), tab)
+        dist.append(err)
     return tab, dist
 
 

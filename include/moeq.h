@@ -64,6 +64,11 @@ enum moeq_status {
 enum moeq_gating { MOEQ_GATING_SOFTMAX_TOPK = 0, MOEQ_GATING_SIGMOID_TOPK = 1 };
 
 #define MOEQ_MAX_EXPERTS 256
+/* At most 4 decode tables per call. Every workgroup of the projection kernels expands each
+ * table into exact bf16 magnitudes for all 256 scale bytes (256 x 16 bytes = 4 KiB of LDS per
+ * table) before it decodes; in the many-rows kernels the activation and code staging buffers
+ * take 128 KiB of the CU's 160 KiB, which leaves room for 4 tables (16 KiB). The pages use two
+ * per layer (the fitted grid and E2M1). */
 #define MOEQ_MAX_TABLES 4
 
 /* Position of intermediate channel c inside a row of `inter` (see moeq_gateup_swiglu):
@@ -286,8 +291,8 @@ int moeq_moe_decode_check(const void* ws, void* stream);
 
 /*
  * Encode bf16 expert weights into the 4-bit format (GLM-5.2-NF4-Lloyd-Experts-GPTQ model card,
- * "Codes are indices into the per-layer grid": the grid is not amax-normalised; a block of 32
- * weights along K is packed against gmax * 2^e >= amax and stores the byte e + 127; "Contents":
+ * "Codes are indices into the per-layer grid": the grid holds absolute magnitudes and each
+ * block of 32 weights along K has a power-of-two scale, stored as the byte e + 127; "Contents":
  * two codes per byte, the even K in the low nibble). Per block: e is the smallest integer with
  * table[7] * 2^e >= max |w| (clamped to [-127, 127]; an all-zero block gets byte 0, a block
  * holding an Inf or NaN gets byte 255 and zero codes); per weight: bits 0..2 index the
@@ -326,6 +331,19 @@ int moeq_quantize(const uint16_t* w, int E, int N, int K, const float* tables, i
 size_t moeq_lloyd_workspace_bytes(int E, int N);
 int moeq_lloyd_stats(const uint16_t* w, int E, int N, int K, const float* table, float gmax,
                      int accumulate, double* stats, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One Lloyd-Max update from the sums of moeq_lloyd_stats (GLM-5.2-NF4-Lloyd-Experts-GPTQ model
+ * card, "What this is": the grid is a weighted Lloyd-Max fit). HOST arrays: stats [24] as
+ * moeq_lloyd_stats leaves them (copied to the host by the caller), table [8] the magnitudes
+ * the sums were taken against, next [8] out: magnitude m moves to the weighted mean of its
+ * ratios, next[m] = fp32(stats[m] / stats[8 + m]) (fp64 quotient, one rounding to nearest),
+ * or keeps table[m] when no ratio fell to it (stats[8 + m] = 0). sq_error (may be NULL) gets
+ * the weighted squared error of the assignment the sums describe, the sum of stats[16..23]
+ * in index order. next may equal table. Runs on the host; no device work. Errors:
+ * MOEQ_EINVAL for null stats, table or next.
+ */
+int moeq_lloyd_update(const double* stats, const float* table, float* next, double* sq_error);
 
 /*
  * Per-expert choice between two encodings (the model card, "Provenance": each expert's winner
