@@ -1,10 +1,11 @@
 // Encoding bf16 expert weights into the 4-bit format, the weighted Lloyd-Max statistics of a
 // grid fit, and the per-expert choice between two tables (GLM-5.2-NF4-Lloyd-Experts-GPTQ
-// model card: "Codes are indices into the per-layer grid" -- the grid is not
-// amax-normalised, a block of 32 along K is packed against gmax * 2^e >= amax with the byte
-// e + 127; "What this is" -- per-layer magnitudes fitted by weighted Lloyd-Max over the pooled
-// ratios |W / 2^e|, each weighted by (2^e)^2; "Provenance" -- each expert keeps the better of
-// the fitted grid and an E2M1 control arm).
+// model card). "Codes are indices into the per-layer grid": a block of 32 along K takes the
+// least exponent e for which the grid's top magnitude times 2^e reaches the block's largest
+// magnitude, stored as the byte e + 127, and each weight the grid magnitude nearest to
+// |w| / 2^e. "What this is": the layer's magnitudes come from a Lloyd-Max fit to those
+// ratios over all experts' matrices together, a ratio weighted by (2^e)^2. "Provenance":
+// each expert keeps whichever of the fitted grid and an E2M1 control table encodes it better.
 //
 // One wavefront per weight row, 16 blocks of 32 at a time: lane l holds 8 weights (one
 // 16-byte load; the wavefront reads 1 KiB of the row contiguously) of block l / 4, the four

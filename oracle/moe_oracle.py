@@ -8,8 +8,9 @@ Sources (the pages' titles; the section named on each function):
 
 * [card]  GLM-5.2-NF4-Lloyd-Experts-GPTQ model card (aidendle94): the storage format --
   "Contents" (4-bit codes + E8M0 block scales, block 32 along K, low nibble = even K) and
-  "Codes are indices into the per-layer grid" (mag = code & 7, sign from bit 3,
-  w = sign * grid[mag] * 2^(scale_byte - 127); the grid is not amax-normalised) and
+  "Codes are indices into the per-layer grid" (the low 3 bits of a code pick one of the 8
+  grid magnitudes, bit 3 is the sign, and the block's scale byte s multiplies by
+  2^(s - 127); the grid holds absolute magnitudes, with no per-block normalisation) and
   "What this is" (the E2M1 table {0, .5, 1, 1.5, 2, 3, 4, 6}).
 * [brief] "Round 7 -- Rewrite the GLM-5.2 routed-expert encoder" (CODEX_ROUND7.md of
   GLM-5.2-EXL3-TR3v4-3.5bpw-MTP78): model geometry (256 routed experts, top-8, hidden 6144,
@@ -248,10 +249,11 @@ def _expert_dense(codes, scales, table):
 def block_scale_bytes(w_bits, gmax: float) -> np.ndarray:
     """Scale byte of every block of 32 along K of bf16 weights [..., K].
 
-    [card] "Codes are indices into the per-layer grid": the grid is not amax-normalised, the
-    codes were packed against gmax * 2^e >= amax; the byte is e + 127 for the smallest such
-    integer e. Readings: e is clamped to [-127, 127]; an all-zero block gets byte 0; a block
-    holding an Inf or NaN gets byte 255 (it decodes to NaN).
+    [card] "Codes are indices into the per-layer grid": a block's exponent e is the least
+    integer for which the grid's top magnitude times 2^e reaches the block's largest
+    magnitude, stored as the byte e + 127. Readings: e is clamped to [-127, 127]; an
+    all-zero block gets byte 0; a block holding an Inf or NaN gets byte 255 (it decodes to
+    NaN).
     """
     w = bf16_to_f64(w_bits)
     blocks = w.reshape(w.shape[:-1] + (w.shape[-1] // 32, 32))
@@ -311,9 +313,10 @@ def reconstruction_sq_error(w_bits, codes, scales, table) -> np.ndarray:
 def lloyd_stats(w_bits, table, gmax=None):
     """One weighted Lloyd-Max step's sums over bf16 weights [N, K] for 8 ascending magnitudes.
 
-    [card] "What this is": per-layer 8-magnitude codebooks fitted by weighted Lloyd-Max over
-    the pooled ratios |W / 2^e| of all experts' gate, up and down weights, each ratio weighted
-    by (2^e)^2 (its share of weight-space squared error). e is each block's exponent for the
+    [card] "What this is": the layer's 8 magnitudes come from a Lloyd-Max fit to the
+    block-normalised magnitudes r = |W| / 2^e of every expert's three matrices taken together,
+    where a ratio counts with weight (2^e)^2, the factor by which its squared error scales back
+    to weight space. e is each block's exponent for the
     top magnitude gmax (block_scale_bytes; default table[7]) and each ratio goes to its
     nearest magnitude of `table` (the rtn_encode rule). Returns float64 [3, 8]: per magnitude
     m, sum (2^e)^2 r, sum (2^e)^2 and sum (2^e)^2 (r - table[m])^2 over the ratios it holds.

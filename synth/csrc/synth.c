@@ -14,8 +14,8 @@
  * 2i (cosine branch) and 2i+1 (sine branch) of the logical matrix.
  *
  * Encoding rule (GLM-5.2-NF4-Lloyd-Experts-GPTQ model card, "Codes are indices into the
- * per-layer grid"): the grid is not amax-normalised; a block of 32 weights along K gets the
- * smallest power of two 2^e with gmax * 2^e >= amax, is stored as byte e + 127, and each
+ * per-layer grid"): the grid holds absolute magnitudes; a block of 32 weights along K gets
+ * the smallest power of two 2^e with gmax * 2^e >= amax, is stored as byte e + 127, and each
  * weight stores the index of its nearest grid magnitude in bits 0..2 and its sign in bit 3.
  * Ties between two magnitudes go to the lower index; a block whose amax is 0 gets byte 0
  * and all-zero codes. Two codes per byte: the even K index in the low nibble ("Contents").
