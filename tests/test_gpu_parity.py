@@ -10,6 +10,7 @@ import torch
 
 import oracle
 import synth
+from inter_check import check_inter
 
 pytestmark = pytest.mark.gpu
 
@@ -73,7 +74,9 @@ def unslot(inter, I):
     return inter[:, _mq().inter_slot(np.arange(I))]
 
 
-def check_layer(out, ref, k, tokens=None, inter_rows=True):
+def check_layer(out, ref, k, lw, x, tokens=None, inter_rows=True):
+    """Routing and permutation bit-exact, gate values to fp32 rounding, the intermediate
+    element-wise (inter_check), y within the row-relative bar; rows of `tokens` (default all)."""
     np.testing.assert_array_equal(out["ids"], ref["ids"])
     np.testing.assert_allclose(out["w"], ref["w"], rtol=2e-6, atol=1e-7)
     np.testing.assert_array_equal(out["offsets"], ref["offsets"])
@@ -84,10 +87,9 @@ def check_layer(out, ref, k, tokens=None, inter_rows=True):
     if inter_rows:
         I = ref["inter"].shape[1]
         rows = ref["pair_pos"].reshape(T, k)[toks].ravel()
-        gi = oracle.bf16_to_f64(unslot(out["inter"], I)[rows])
-        ri = oracle.bf16_to_f64(ref["inter"][rows])
-        rel_i = np.linalg.norm(gi - ri, axis=1) / np.linalg.norm(ri, axis=1)
-        assert rel_i.max() < ROW_REL_TOL, rel_i.max()
+        pairs = ref["sorted_pair"][rows]
+        check_inter(unslot(out["inter"], I)[rows], ref["inter"][rows], pairs // k,
+                    ref["ids"].ravel()[pairs], x, lw, label=f"{T} tokens")
     rel = row_rel(out["y"][toks], ref["y"][toks])
     assert np.all(np.isfinite(rel)) and rel.max() <= ROW_REL_TOL, rel.max()
     return rel.max()
@@ -253,7 +255,7 @@ def test_layer_routed_sigmoid(path):
     assert np.all(np.abs(gl - oracle.router_logits(x, wr)) <= _router_bound(x, wr))
     routing = oracle.route_topk(gl, k, "sigmoid")
     ref = oracle.layer_forward(x, gl, k, lw, routing=routing)
-    check_layer(out, ref, k)
+    check_layer(out, ref, k, lw, x)
 
 
 @pytest.mark.parametrize("T,k,E", [(16, 2, 4), (8, 8, 256), (2048, 8, 256), (8192, 8, 256),
@@ -306,6 +308,7 @@ def test_permute_invalid_ids_small(P, E):
     np.testing.assert_array_equal(host(pp), rp)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("P,E", [(4096, 256), (4097, 17), (40000, 256), (65536 + 1000, 64)])
 def test_permute_many_pairs_with_invalid_ids(P, E):
     """The three-launch form (blocks of 1024 pairs, the last one larger), skewed ids and
@@ -342,7 +345,7 @@ def test_layer_tiny_config(path):
     lw, x, logits = _case(1, c.T, c.E, c.H, c.I, c.k)
     out = run_layer(lw, x, logits, c.k)
     ref = oracle.layer_forward(x, logits, c.k, lw)
-    check_layer(out, ref, c.k)
+    check_layer(out, ref, c.k, lw, x)
 
 
 def test_layer_empty_batch(path):
@@ -374,7 +377,7 @@ def test_layer_ragged_shapes(T, E, H, I, k, path):
     lw, x, logits = _case(21, T, E, H, I, k, e2m1_experts=(1,), permute="random")
     out = run_layer(lw, x, logits, k)
     ref = oracle.layer_forward(x, logits, k, lw)
-    check_layer(out, ref, k)
+    check_layer(out, ref, k, lw, x)
 
 
 @pytest.mark.parametrize("groups", [1, 3])
@@ -388,7 +391,7 @@ def test_layer_prefill_few_workgroups(T, E, H, I, k, groups, monkeypatch):
     lw, x, logits = _case(24, T, E, H, I, k, e2m1_experts=(1,), permute="random")
     out = run_layer(lw, x, logits, k)
     ref = oracle.layer_forward(x, logits, k, lw)
-    check_layer(out, ref, k)
+    check_layer(out, ref, k, lw, x)
 
 
 def test_layer_residual_in_place(path):
@@ -458,53 +461,102 @@ def glm_layer():
     return synth.make_layer(2, c.E, c.H, c.I)
 
 
+@pytest.mark.timeout(600)
 def test_glm_decode_t8_full(glm_layer):
     c = synth.WORKLOADS["glm_decode_t8"]
     x = synth.make_x(2, c.T, c.H)
     logits = synth.make_logits(2, c.T, c.E)
     out = run_layer(glm_layer, x, logits, c.k)
     ref = oracle.layer_forward(x, logits, c.k, glm_layer)
-    check_layer(out, ref, c.k)
+    check_layer(out, ref, c.k, glm_layer, x)
 
 
-def _sample_tokens(ids, n, seed):
-    """n tokens: the ones routed to the most-loaded expert first, then random ones."""
-    counts = np.bincount(ids.ravel(), minlength=256)
+def _tile_class_tokens(out, k, seed, n_random=1):
+    """Tokens whose pairs sit at every tile class of the most-loaded expert under the 128-row
+    tiles of the many-rows kernels (the first row of its first tile, the last row of its
+    first full tile, the first and the last row of its last tile, partial when its row count
+    is not a multiple of 128), a token on the least-loaded expert (at most 32 rows: a tile
+    whose 32-row MFMA tiles are mostly skipped), and random tokens. Returns (tokens, hot)."""
+    off, sp = out["offsets"], out["sorted_pair"]
+    counts = np.diff(off)
     hot = int(np.argmax(counts))
-    on_hot = np.where((ids == hot).any(1))[0]
+    b, n = int(off[hot]), int(counts[hot])
+    rows = {b, b + min(127, n - 1), b + (n - 1) // 128 * 128, b + n - 1}
+    toks = {int(sp[r]) // k for r in rows}
+    live = np.flatnonzero(counts > 0)
+    small = int(live[np.argmin(counts[live])])
+    assert counts[small] <= 32
+    toks.add(int(sp[off[small]]) // k)
     g = np.random.default_rng(seed)
-    pick = list(g.choice(on_hot, size=min(2, len(on_hot)), replace=False))
-    rest = np.setdiff1d(np.arange(ids.shape[0]), pick)
-    pick += list(g.choice(rest, size=n - len(pick), replace=False))
-    return sorted(int(t) for t in pick)
+    rest = np.setdiff1d(np.arange(out["y"].shape[0]), sorted(toks))
+    toks |= {int(t) for t in g.choice(rest, size=n_random, replace=False)}
+    return sorted(toks), hot
 
 
+def _check_expert_rows(out, x, lw, k, e, label):
+    """The intermediate of every row of expert e, element-wise against the oracle."""
+    off, sp = out["offsets"], out["sorted_pair"]
+    rows = np.arange(off[e], off[e + 1])
+    assert rows.size > 0
+    toks = sp[rows] // k
+    I = lw.gate_codes.shape[1]
+    ref = oracle.expert_inter(x, lw, e, toks)
+    check_inter(unslot(out["inter"], I)[rows], ref, toks, np.full(rows.size, e), x, lw,
+                label=f"{label}: expert {e}, {rows.size} rows")
+
+
+@pytest.mark.timeout(600)
 def test_glm_prefill_t2048_zipf_sampled():
+    """2048 tokens under Zipf routing: every row of the hottest expert (16 tiles of the
+    many-rows kernels) element-wise, y of tokens at each of its tile classes and on the
+    least-loaded expert; then the rank-1 Zipf expert re-packed on the E2M1 grid (its table
+    id set to E2M1), which must route identically and give its rows from the E2M1 table."""
     c = synth.WORKLOADS["glm_prefill_t2048_zipf"]
     lw = synth.make_layer(3, c.E, c.H, c.I)
     x = synth.make_x(3, c.T, c.H)
     logits = synth.make_logits(3, c.T, c.E, zipf_s=c.zipf_s)
     out = run_layer(lw, x, logits, c.k)
-    toks = _sample_tokens(out["ids"], 5, 3)
+    toks, hot = _tile_class_tokens(out, c.k, 3)
+    _check_expert_rows(out, x, lw, c.k, hot, "hottest")
     ref = oracle.layer_forward(x, logits, c.k, lw, tokens=toks)
-    check_layer(out, ref, c.k, tokens=toks)
+    check_layer(out, ref, c.k, lw, x, tokens=toks)
+
+    e1 = int(np.argmax(synth.zipf_bias(3, c.E, c.zipf_s)))        # rank 1 of the Zipf bias
+    sub = synth.make_layer(3, c.E, c.H, c.I, e2m1_experts=(e1,), experts=[e1])
+    for name in ("gate_codes", "gate_scales", "up_codes", "up_scales", "down_codes",
+                 "down_scales"):
+        getattr(lw, name)[e1] = getattr(sub, name)[e1]
+    lw.table_id[e1] = 1
+    out2 = run_layer(lw, x, logits, c.k)
+    np.testing.assert_array_equal(out2["sorted_pair"], out["sorted_pair"])
+    assert np.diff(out2["offsets"])[e1] > 128
+    _check_expert_rows(out2, x, lw, c.k, e1, "rank-1 on E2M1")
+    t1 = [int(out2["sorted_pair"][out2["offsets"][e1 + 1] - 1]) // c.k]
+    ref2 = oracle.layer_forward(x, logits, c.k, lw, tokens=t1)
+    check_layer(out2, ref2, c.k, lw, x, tokens=t1)
 
 
+@pytest.mark.timeout(600)
 def test_glm_prefill_t8192_e2m1_permuted_sampled():
     """8192 tokens, Zipf routing, the E2M1 experts of the model card's defect table and a
-    random intermediate-channel permutation baked into gate-N, up-N and down-K."""
+    random intermediate-channel permutation baked into gate-N, up-N and down-K: every row of
+    the hottest expert and of every E2M1 expert that has rows, element-wise; y of tokens at
+    each tile class of the hottest expert, on the least-loaded expert and on an E2M1 expert."""
     c = synth.WORKLOADS["glm_prefill_t8192_zipf_e2m1_perm"]
     lw = synth.make_layer(5, c.E, c.H, c.I, e2m1_experts=c.e2m1, permute=c.permute)
     x = synth.make_x(5, c.T, c.H)
     logits = synth.make_logits(5, c.T, c.E, zipf_s=c.zipf_s)
     out = run_layer(lw, x, logits, c.k)
-    ids = out["ids"]
-    toks = _sample_tokens(ids, 4, 5)
-    on_e2m1 = np.where(np.isin(ids, list(c.e2m1)).any(1))[0]
-    assert len(on_e2m1) > 0
-    toks = sorted(set(toks) | {int(on_e2m1[0])})
+    toks, hot = _tile_class_tokens(out, c.k, 5)
+    _check_expert_rows(out, x, lw, c.k, hot, "hottest")
+    counts = np.diff(out["offsets"])
+    on = [e for e in c.e2m1 if counts[e] > 0]
+    assert on
+    for e in on:
+        _check_expert_rows(out, x, lw, c.k, e, "E2M1")
+    toks = sorted(set(toks) | {int(out["sorted_pair"][out["offsets"][on[0]]]) // c.k})
     ref = oracle.layer_forward(x, logits, c.k, lw, tokens=toks)
-    check_layer(out, ref, c.k, tokens=toks)
+    check_layer(out, ref, c.k, lw, x, tokens=toks)
 
 
 def test_block_permutation_relayout_gpu(path):
@@ -563,10 +615,8 @@ def test_shared_expert(T, H, I, path):
     x = synth.make_x(41, T, H)
     inter, z = _run_shared(sw, x)
     ref = oracle.shared_expert_forward(x, sw)
-    gi = oracle.bf16_to_f64(unslot(inter, I))
-    ri = oracle.bf16_to_f64(ref["inter"])
-    rel_i = np.linalg.norm(gi - ri, axis=1) / np.linalg.norm(ri, axis=1)
-    assert rel_i.max() < ROW_REL_TOL, rel_i.max()
+    check_inter(unslot(inter, I), ref["inter"], np.arange(T), np.zeros(T, np.int64), x, sw,
+                label="shared expert")
     rel = np.linalg.norm(z - ref["z"], axis=1) / np.linalg.norm(ref["z"], axis=1)
     assert np.all(np.isfinite(z)) and rel.max() <= ROW_REL_TOL, rel.max()
 
@@ -599,6 +649,7 @@ def test_layer_with_shared_expert(T, E, H, I, k, path):
     assert (np.linalg.norm(got - plain, axis=1) / np.linalg.norm(plain, axis=1)).max() > 1e-2
 
 
+@pytest.mark.timeout(600)
 def test_glm_decode_t8_with_shared_expert(glm_layer):
     mq = _mq()
     c = synth.WORKLOADS["glm_decode_t8"]
@@ -688,6 +739,7 @@ def test_lloyd_stats_and_pooling():
     np.testing.assert_allclose(host(stats).reshape(3, 8), ref, rtol=1e-12)
 
 
+@pytest.mark.timeout(600)
 def test_grid_fit_and_layer_encode_end_to_end(path):
     """Fit the grid (weighted Lloyd), choose arms and encode a layer on the GPU; then run the
     encoded layer forward on the GPU: all against the oracle."""
@@ -742,6 +794,7 @@ def test_grid_fit_and_layer_encode_end_to_end(path):
     assert rel.max() <= ROW_REL_TOL, rel.max()
 
 
+@pytest.mark.timeout(600)
 def test_quantize_glm_expert_sampled_rows():
     """A GLM-size expert matrix (2048 x 6144) in the launch the layer encoder uses; sampled
     rows against the oracle."""
@@ -766,6 +819,7 @@ def test_quantize_glm_expert_sampled_rows():
 # the decode layer as one cooperative launch
 # ----------------------------------------------------------------------------------------------
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("T,E,H,I,k,gating", [(16, 4, 256, 128, 2, 0), (37, 8, 576, 320, 4, 1),
                                               (1, 16, 256, 128, 16, 0), (8, 256, 6144, 2048, 8, 0),
                                               (64, 256, 6144, 2048, 8, 1)])
@@ -789,11 +843,15 @@ def test_moe_decode_single_launch(T, E, H, I, k, gating, monkeypatch):
         y = L.forward_fused(xb, lg, w, residual=xb, out=xb)            # in place over x
         mq.moeq_moe_decode_check(L.f_ws)
         np.testing.assert_array_equal(u16(y), ref_bits)
-        # the oracle on the small shapes and the 8-token GLM layer (the bit-identity above ties
-        # the rest to the per-step calls, which their own tests hold to the oracle)
-        if H != 6144 or (call == 0 and T <= 8):
+        # the oracle on the small shapes and on the first call of the GLM layers (all 8
+        # tokens; the first and last of 64); the bit-identity above ties the rest to the
+        # per-step calls, which their own tests hold to the oracle
+        if H != 6144 or call == 0:
             routing = oracle.route_topk(logits, k, "sigmoid" if gating else "softmax")
-            tokens = None if T <= 16 else list(range(0, T, 9))
+            if T <= 16:
+                tokens = None
+            else:
+                tokens = [0, T - 1] if H == 6144 else list(range(0, T, 9))
             ref = oracle.layer_forward(x, logits, k, lw, residual_bits=x, routing=routing,
                                        tokens=tokens)
             toks = np.arange(T) if tokens is None else np.asarray(tokens)

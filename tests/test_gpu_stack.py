@@ -32,6 +32,7 @@ def _rows_rel(gpu_bits, ref):
     return np.linalg.norm(g - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-300)
 
 
+@pytest.mark.timeout(300)
 def test_stack_free_running_small():
     """16 layers of a small shape (H 256, I 128, E 16, top-2, 24 tokens), residual in place,
     against the oracle's free-running stack."""
