@@ -27,11 +27,13 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MOEQ_OK, MOEQ_EINVAL, MOEQ_EUNSUPPORTED, MOEQ_EWORKSPACE, MOEQ_ELAUNCH = 0, -1, -2, -3, -4
 MOEQ_GATING_SOFTMAX_TOPK, MOEQ_GATING_SIGMOID_TOPK = 0, 1
+MOEQ_STATIC_SCRATCH_BYTES = (32 << 20) + 256    # include/moeq.h
 MAX_EXPERTS = 256
 MAX_TABLES = 4
 
 EXPORTED = ("moeq_last_error", "moeq_workspace_bytes", "moeq_router_logits", "moeq_route_topk",
-            "moeq_permute_by_expert", "moeq_route_permute", "moeq_gateup_swiglu", "moeq_down",
+            "moeq_permute_by_expert", "moeq_route_permute", "moeq_gateup_swiglu",
+            "moeq_gateup_swiglu_static", "moeq_down",
             "moeq_unpermute_combine", "moeq_shared_workspace_bytes", "moeq_shared_expert",
             "moeq_unpermute_combine_shared", "moeq_quantize", "moeq_lloyd_workspace_bytes",
             "moeq_lloyd_stats", "moeq_lloyd_update", "moeq_select_arms",
@@ -54,6 +56,9 @@ _lib.moeq_permute_by_expert.argtypes = [_vp, _i, _i, _i, _vp, _vp, _vp, _vp]
 _lib.moeq_gateup_swiglu.restype = _i
 _lib.moeq_gateup_swiglu.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _i, _vp, _vp, _vp, _sz, _vp]
+_lib.moeq_gateup_swiglu_static.restype = _i
+_lib.moeq_gateup_swiglu_static.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
+                                           _vp, _vp, _i, _vp, _vp, _vp]
 _lib.moeq_down.restype = _i
 _lib.moeq_down.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp,
                            _vp, _sz, _vp]
@@ -165,6 +170,16 @@ def moeq_gateup_swiglu(x, T, H, I, E, k, expert_offsets, sorted_pair, gate_codes
                                    _p(gate_codes), _p(gate_scales), _p(up_codes), _p(up_scales),
                                    tab.ctypes.data, n, _p(table_id), _p(inter), _p(ws), ws_bytes,
                                    _stream(stream)))
+
+
+def moeq_gateup_swiglu_static(x, T, H, I, E, k, expert_offsets, sorted_pair, gate_codes,
+                              gate_scales, up_codes, up_scales, tables, table_id, inter,
+                              stream=None):
+    tab, n = _tables(tables)
+    _check(_lib.moeq_gateup_swiglu_static(_p(x), T, H, I, E, k, _p(expert_offsets),
+                                          _p(sorted_pair), _p(gate_codes), _p(gate_scales),
+                                          _p(up_codes), _p(up_scales), tab.ctypes.data, n,
+                                          _p(table_id), _p(inter), _stream(stream)))
 
 
 def moeq_down(inter, T, H, I, E, k, expert_offsets, sorted_pair, topk_w, down_codes,

@@ -7,6 +7,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moeq.h"
 #include "moeq_kernels.h"
 
@@ -277,6 +279,63 @@ int moeq_gateup_swiglu(const uint16_t* x, int T, int H, int I, int E, int k,
     return projection("moeq_gateup_swiglu", true, x, T, H, I, E, k, expert_offsets, sorted_pair,
                       nullptr, gate_codes, gate_scales, up_codes, up_scales, tables, n_tables,
                       table_id, inter, ws, ws_bytes, (hipStream_t)stream);
+}
+
+// The static scratch of moeq_gateup_swiglu_static. In host code `scratch` is only a stand-in
+// for the symbol: its device address on the current device comes from hipGetSymbolAddress
+// (each device holds its own copy), kept per device in g_scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[MOEQ_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up on the first call there.
+int static_scratch(const char* w, void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        clear_hip_error();
+        return fail(MOEQ_ELAUNCH, "%s: no current device (or device id %d >= %d)", w, dev,
+                    kMaxDevices);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            clear_hip_error();
+            return fail(MOEQ_ELAUNCH, "%s: the static scratch has no address on device %d: %s",
+                        w, dev, hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOEQ_OK;
+}
+}  // namespace
+
+int moeq_gateup_swiglu_static(const uint16_t* x, int T, int H, int I, int E, int k,
+                              const int32_t* expert_offsets, const int32_t* sorted_pair,
+                              const uint8_t* gate_codes, const uint8_t* gate_scales,
+                              const uint8_t* up_codes, const uint8_t* up_scales,
+                              const float* tables, int n_tables, const uint8_t* table_id,
+                              uint16_t* inter, void* stream) {
+    const char* w = "moeq_gateup_swiglu_static";
+    if (T > 0 && H > 0) {
+        const size_t need = moeq_workspace_bytes(T, k, E, H, I);
+        if (need > MOEQ_STATIC_SCRATCH_BYTES)
+            return fail(MOEQ_EWORKSPACE,
+                        "%s: T = %d, H = %d need %zu bytes of scratch, above the static %zu "
+                        "(use moeq_gateup_swiglu with a workspace)",
+                        w, T, H, need, (size_t)MOEQ_STATIC_SCRATCH_BYTES);
+    }
+    void* ws = nullptr;
+    if (T > 0)
+        if (int r = static_scratch(w, &ws)) return r;
+    return projection(w, true, x, T, H, I, E, k, expert_offsets, sorted_pair, nullptr,
+                      gate_codes, gate_scales, up_codes, up_scales, tables, n_tables, table_id,
+                      inter, ws, MOEQ_STATIC_SCRATCH_BYTES, (hipStream_t)stream);
 }
 
 int moeq_down(const uint16_t* inter, int T, int H, int I, int E, int k,

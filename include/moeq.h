@@ -181,6 +181,31 @@ int moeq_gateup_swiglu(const uint16_t* x, int T, int H, int I, int E, int k,
                        int n_tables, const uint8_t* table_id, uint16_t* inter, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* Length of the library's static scratch array: the most scratch moeq_gateup_swiglu_static
+ * can use. 32 MiB + 256 bytes covers moeq_workspace_bytes for T * H <= 16,777,216, e.g. up to
+ * 2730 tokens at H = 6144. */
+#define MOEQ_STATIC_SCRATCH_BYTES (((size_t)32 << 20) + 256)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): moeq_gateup_swiglu without the workspace
+ * arguments. Its scratch (moeq_workspace_bytes(T, k, E, H, I) bytes: the work-queue counters
+ * and the pair-split copy of x) lives in a static device array of this library,
+ * MOEQ_STATIC_SCRATCH_BYTES long, which every GPU the library runs on holds until the process
+ * ends. The call allocates nothing; its first call on a device looks that array's address up
+ * on the device. Arguments, kernels and results are those of moeq_gateup_swiglu.
+ * Calls that overlap on one GPU (other streams, other threads) share the array and race:
+ * serialise them. Each call clears what must start at zero itself (on its stream).
+ * Errors: as moeq_gateup_swiglu; MOEQ_EWORKSPACE, with nothing launched, when the call needs
+ * more than MOEQ_STATIC_SCRATCH_BYTES; MOEQ_ELAUNCH when the array's address cannot be found.
+ */
+int moeq_gateup_swiglu_static(const uint16_t* x, int T, int H, int I, int E, int k,
+                              const int32_t* expert_offsets, const int32_t* sorted_pair,
+                              const uint8_t* gate_codes, const uint8_t* gate_scales,
+                              const uint8_t* up_codes, const uint8_t* up_scales,
+                              const float* tables, int n_tables, const uint8_t* table_id,
+                              uint16_t* inter, void* stream);
+
 /*
  * Down projection with the gate weight applied ("Round 7" brief, decision 6; README of
  * GLM-5.2-EXL3-TR3v4-3.5bpw-MTP78, "What had to be fixed": router weighting happens in the
