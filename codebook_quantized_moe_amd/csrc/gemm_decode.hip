@@ -272,14 +272,15 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
         return sr;
     };
     // codes of K-step st: lane (b, q) of group g reads 32 codes of row 4 g + q at K 32 b
-    auto load_step = [&](const Src& sr, int st, u32x4 (&c)[4]) {
+    auto load_group = [&](const Src& sr, int st, int g) {
         const int kk = st * kStepK;
         const bool ok = kk + b * 32 < K;
+        const uint32_t off = (ok && sr.off[g] != kOutOfRange) ? sr.off[g] + kk / 2 : kOutOfRange;
+        return bload16<kStreamPolicy>((GATEUP && g >= 2) ? sr.c1 : sr.c0, off);
+    };
+    auto load_step = [&](const Src& sr, int st, u32x4 (&c)[4]) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const uint32_t off = (ok && sr.off[g] != kOutOfRange) ? sr.off[g] + kk / 2 : kOutOfRange;
-            c[g] = bload16<kStreamPolicy>((GATEUP && g >= 2) ? sr.c1 : sr.c0, off);
-        }
+        for (int g = 0; g < 4; ++g) c[g] = load_group(sr, st, g);
     };
 
     // ---------------- staging of activations and scales (per workgroup, per chunk) -------
@@ -348,19 +349,22 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
 
     // ---------------- main loop ----------------
     // Per chunk of kSteps K-steps: the next chunk (of this item or the next one) is staged by
-    // DMA into the other buffers; the codes of each K-step were loaded one K-step ahead into
-    // one of two register slots (cA for even steps, cB for odd ones); after the chunk the DMA
-    // is waited for (the 4 kSteps code loads issued after it may stay in flight) and one
-    // barrier switches the buffers.
+    // DMA into the other buffers; the codes of K-step s sit in one of two register slots (cA
+    // for even steps, cB for odd ones), and as soon as group g of step s is decoded its
+    // registers take the load of group g of step s + 2 (of this item or the next): about one
+    // and a half K-steps of codes stay in flight per wavefront, with no register beyond the two
+    // slots. After the chunk the DMA is waited for (the 4 kSteps code loads issued after it may
+    // stay in flight) and one barrier switches the buffers.
     constexpr int kSteps = kChunkK / kStepK;
-    static_assert(kSteps % 2 == 0, "even K-steps per chunk");
+    static_assert(kSteps % 2 == 0 && kSteps >= 2, "even K-steps per chunk");
     const int nchunks = nsteps / kSteps;
     Src cur = make_src(first);
     Src nxt = make_src(first + stride);
     stage_dma(cur, 0, 0);
     u32x4 cA[4], cB[4];
     load_step(cur, 0, cA);
-    MOEQ_DEC_WAIT_VMCNT(4);        // the staging has landed; the 4 code loads may be in flight
+    load_step(cur, 1, cB);         // an item has at least kSteps >= 2 K-steps
+    MOEQ_DEC_WAIT_VMCNT(8);        // the staging has landed; the 8 code loads may be in flight
     __syncthreads();
     int buf = 0;
 
@@ -378,7 +382,8 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
             soff[g] = SALIGN ? R * kSRow : R * kSRow + (int)(((uint32_t)wrow * ks) & 15u);
             acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        auto compute = [&](const u32x4 (&c)[4], int kk) {
+        // step kk / kStepK from slot c; group g's registers then load step rst of rs
+        auto compute = [&](u32x4 (&c)[4], int kk, const Src& rs, int rst) {
             // activation operands: tile row q, K 32 b .. 32 b + 31 of the step (pair-split)
             const uint8_t* ap = abuf + buf * kABufBytes + q * kARowUnits * 16 +
                                 ((kk % kChunkK) / 8 + b * 4) * 16;
@@ -403,6 +408,7 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
                     acc[g] = mfma4x4x4(A[j][0], A[j][1], w[0], w[1], acc[g]);
                     acc[g] = mfma4x4x4(A[j][2], A[j][3], w[2], w[3], acc[g]);
                 }
+                c[g] = load_group(rs, rst, g);
             }
         };
         for (int ch = 0; ch < nchunks; ++ch) {
@@ -412,9 +418,11 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
 #pragma unroll
             for (int j = 0; j < kSteps; ++j) {
                 const int st = ch * kSteps + j;
-                if (j + 1 < kSteps) load_step(cur, st + 1, (j & 1) ? cA : cB);
-                else load_step(ns, lastc ? 0 : st + 1, (j & 1) ? cA : cB);
-                compute((j & 1) ? cB : cA, st * kStepK);
+                // step st + 2: in this item, or (last chunk, last two steps) step j + 2 - kSteps
+                // of the next one
+                const bool nx = lastc && j + 2 >= kSteps;
+                compute((j & 1) ? cB : cA, st * kStepK, nx ? nxt : cur,
+                        nx ? j + 2 - kSteps : st + 2);
             }
             MOEQ_DEC_WAIT_VMCNT(4 * kSteps);
             __syncthreads();
