@@ -10,10 +10,14 @@
 // One wavefront per weight row, 16 blocks of 32 at a time: lane l holds 8 weights (one
 // 16-byte load; the wavefront reads 1 KiB of the row contiguously) of block l / 4, the four
 // lanes of a block agree on its maximum through two DPP swaps, and each stores its 4 code
-// bytes (64 lanes: 256 contiguous bytes). The ratio |w| / 2^e of a bf16 weight is exact in fp64, and so are the
-// midpoints of two fp32 magnitudes, so the nearest-magnitude decision (ties to the lower) is
-// exact. Sums are fp64, each lane's in block order, then across lanes in a fixed butterfly,
-// then across rows in row order: the same inputs give the same bits.
+// bytes (64 lanes: 256 contiguous bytes). The ratio |w| / 2^e of a bf16 weight is exact in
+// fp64, and so are the midpoints of two fp32 magnitudes, so the nearest-magnitude decision
+// (ties to the lower) is exact. It is taken in fp32 where that is exact too: the ratio is an
+// fp32 value unless it falls below the normal range (then fp64 decides), and for an fp32 r,
+// r > m exactly when r is above the largest fp32 value not above m. The kernel is specialised
+// on its outputs (codes and scales, row errors, or both), so the packing pass does no error
+// work. Sums are fp64, each lane's in block order, then across lanes in a fixed butterfly, then
+// across rows in row order: the same inputs give the same bits.
 #include "moeq_device.h"
 #include "moeq_kernels.h"
 
@@ -80,6 +84,18 @@ __device__ __forceinline__ int nearest(double r, const double (&mid)[7]) {
     return m;
 }
 
+// index of the magnitude nearest to an fp32 ratio r, exact when r is: for an fp32 value r and a
+// real midpoint m, r > m exactly when r > the largest fp32 value not above m (mid32)
+__device__ __forceinline__ int nearest32(float r, const float (&mid32)[7]) {
+    int m = 0;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) m += r > mid32[i];
+    return m;
+}
+
+// CODES: write codes and/or scales (whichever is given); ERR: the row's squared reconstruction
+// error (either or both)
+template <bool CODES, bool ERR>
 __global__ void __launch_bounds__(kQThreads) quantize_kernel(const uint16_t* __restrict__ w,
                                                              long long rows, int K, int N,
                                                              TableArgs ta,
@@ -94,10 +110,16 @@ __global__ void __launch_bounds__(kQThreads) quantize_kernel(const uint16_t* __r
     const bool badtab = t >= ta.n;
     float g[8];
     double mid[7];
+    float mid32[7];
 #pragma unroll
     for (int m = 0; m < 8; ++m) g[m] = badtab ? 0.f : ta.v[t][m];
 #pragma unroll
-    for (int i = 0; i < 7; ++i) mid[i] = 0.5 * ((double)g[i] + (double)g[i + 1]);
+    for (int i = 0; i < 7; ++i) {
+        mid[i] = 0.5 * ((double)g[i] + (double)g[i + 1]);          // exact in fp64
+        float f = (float)mid[i];
+        if ((double)f > mid[i]) f = __uint_as_float(__float_as_uint(f) - 1u);   // f > 0 here
+        mid32[i] = f;
+    }
     const uint16_t* wr = w + (size_t)row * K;
     const int nb = K / 32;
     const int q = lane & 3;
@@ -108,15 +130,19 @@ __global__ void __launch_bounds__(kQThreads) quantize_kernel(const uint16_t* __r
         // an unknown table id encodes NaN blocks (gmax is then 0: block_code gives 255)
         const BlockCode bc = block_code(quad_amax(h), g[7]);
         const double inv = ldexp(1.0, -bc.e);
+        const float invf = (float)inv;                              // a power of two: exact
         // the block's 8 reconstructions bf16(g[m] * 2^e): lane q of the quad forms those of
         // magnitudes 2q and 2q + 1, and four DPP broadcasts give every lane all four pairs
-        const float ga = q == 0 ? g[0] : q == 1 ? g[2] : q == 2 ? g[4] : g[6];
-        const float gb = q == 0 ? g[1] : q == 1 ? g[3] : q == 2 ? g[5] : g[7];
-        const int own = (int)(scaled_bf16_bits(ga, bc.s) | (scaled_bf16_bits(gb, bc.s) << 16));
-        const uint32_t pr[4] = {(uint32_t)__builtin_amdgcn_update_dpp(0, own, 0x00, 0xF, 0xF, false),
-                                (uint32_t)__builtin_amdgcn_update_dpp(0, own, 0x55, 0xF, 0xF, false),
-                                (uint32_t)__builtin_amdgcn_update_dpp(0, own, 0xAA, 0xF, 0xF, false),
-                                (uint32_t)__builtin_amdgcn_update_dpp(0, own, 0xFF, 0xF, 0xF, false)};
+        uint32_t pr[4] = {0u, 0u, 0u, 0u};
+        if (ERR) {
+            const float ga = q == 0 ? g[0] : q == 1 ? g[2] : q == 2 ? g[4] : g[6];
+            const float gb = q == 0 ? g[1] : q == 1 ? g[3] : q == 2 ? g[5] : g[7];
+            const int own = (int)(scaled_bf16_bits(ga, bc.s) | (scaled_bf16_bits(gb, bc.s) << 16));
+            pr[0] = (uint32_t)__builtin_amdgcn_update_dpp(0, own, 0x00, 0xF, 0xF, false);
+            pr[1] = (uint32_t)__builtin_amdgcn_update_dpp(0, own, 0x55, 0xF, 0xF, false);
+            pr[2] = (uint32_t)__builtin_amdgcn_update_dpp(0, own, 0xAA, 0xF, 0xF, false);
+            pr[3] = (uint32_t)__builtin_amdgcn_update_dpp(0, own, 0xFF, 0xF, 0xF, false);
+        }
         if (b >= nb) continue;
         uint32_t packed = 0u;
 #pragma unroll
@@ -124,23 +150,34 @@ __global__ void __launch_bounds__(kQThreads) quantize_kernel(const uint16_t* __r
             const uint32_t hb = (h[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
             const uint32_t mag_bits = hb & 0x7FFFu;
             const bool neg = (hb & 0x8000u) && mag_bits != 0;
-            const double x = (double)bf16_to_f32(hb);
-            const int m = nearest((double)bf16_to_f32(mag_bits) * inv, mid);
-            const uint32_t pm = m < 2 ? pr[0] : m < 4 ? pr[1] : m < 6 ? pr[2] : pr[3];
-            const float rm = bf16_to_f32((m & 1) ? pm >> 16 : pm & 0xFFFFu);
-            const double d = x - (neg ? -(double)rm : (double)rm);
-            err += d * d;
+            // |w| / 2^e is a bf16 value times a power of two: exact in fp32 unless it falls
+            // below the normal range, where the decision is taken in fp64
+            const float magf = bf16_to_f32(mag_bits);
+            const float rf = magf * invf;
+            int m = nearest32(rf, mid32);
+            if (rf < 0x1p-126f && mag_bits != 0) m = nearest((double)magf * inv, mid);
+            if (ERR) {
+                const double x = (double)bf16_to_f32(hb);
+                const uint32_t pm = m < 2 ? pr[0] : m < 4 ? pr[1] : m < 6 ? pr[2] : pr[3];
+                const float rm = bf16_to_f32((m & 1) ? pm >> 16 : pm & 0xFFFFu);
+                const double d = x - (neg ? -(double)rm : (double)rm);
+                err += d * d;
+            }
             const uint32_t code = bc.s == 255 ? 0u : (uint32_t)m | (neg ? 8u : 0u);
             packed |= code << (4 * j);
         }
-        if (bc.s == 255) err += __builtin_nan("");
-        if (codes)
-            *reinterpret_cast<uint32_t*>(codes + (size_t)row * (K / 2) + (size_t)b * 16 + q * 4) =
-                packed;
-        if (scales && q == 0) scales[(size_t)row * nb + b] = (uint8_t)bc.s;
+        if (ERR && bc.s == 255) err += __builtin_nan("");
+        if (CODES) {
+            if (codes)
+                *reinterpret_cast<uint32_t*>(codes + (size_t)row * (K / 2) + (size_t)b * 16 + q * 4) =
+                    packed;
+            if (scales && q == 0) scales[(size_t)row * nb + b] = (uint8_t)bc.s;
+        }
     }
-    err = wave_sum_f64(err);
-    if (row_err && lane == 0) row_err[row] = err;
+    if (ERR) {
+        err = wave_sum_f64(err);
+        if (lane == 0) row_err[row] = err;
+    }
 }
 
 // Per workgroup (its 4 waves' rows), 24 fp64 sums: for magnitude m, sum (2^e)^2 r, sum (2^e)^2 and
@@ -260,8 +297,15 @@ void launch_quantize(const uint16_t* w, long long rows, int K, int N, const Tabl
                      const uint8_t* table_id, uint8_t* codes, uint8_t* scales, double* row_err,
                      hipStream_t stream) {
     const long long blocks = (rows + kQWaves - 1) / kQWaves;
-    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(kQThreads), 0, stream, w,
-                       rows, K, N, ta, table_id, codes, scales, row_err);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kQThreads), 0, stream, w, rows, K,
+                           N, ta, table_id, codes, scales, row_err);
+    };
+    // CODES: codes or scales (or both) are written; ERR: row errors
+    const bool want_codes = codes != nullptr || scales != nullptr;
+    if (want_codes && row_err) go(quantize_kernel<true, true>);
+    else if (want_codes) go(quantize_kernel<true, false>);
+    else if (row_err) go(quantize_kernel<false, true>);
 }
 
 // workgroups of the statistics pass: enough to fill the chip (3 per CU by LDS), few enough that
