@@ -711,6 +711,89 @@ def test_quantize_bitexact():
     np.testing.assert_array_equal(host(err2).view(np.uint64), host(err).view(np.uint64))
 
 
+# tables of the boundary test: a Lloyd grid, E2M1, E2M1 scaled far down and up (so that block
+# exponents clamp at +-127 and thresholds reach the ends of the bf16 range), repeated
+# magnitudes, and a table whose first midpoint is 0
+BOUNDARY_TABLES = np.stack([synth.lloyd_grid(1, 0), oracle.E2M1_TABLE,
+                            oracle.E2M1_TABLE * np.float32(2.0 ** -20),
+                            oracle.E2M1_TABLE * np.float32(2.0 ** 20),
+                            np.array([0.1, 0.1, 0.5, 0.5, 0.5, 1, 2, 2], np.float32),
+                            np.array([0, 0, 0, 0, 0, 0, 0, 1], np.float32)]).astype(np.float32)
+
+
+def _boundary_weights(seed, N, K):
+    """bf16 bits [E, N, K], expert t for table t: every block draws its exponent across the
+    whole bf16 range (block maxima from subnormal to near the largest finite value), spreads
+    its other magnitudes over 12 binades below the maximum, and places weights exactly on
+    midpoints times 2^e (ties) and one bf16 step either side of them."""
+    g = np.random.default_rng(seed)
+    E = len(BOUNDARY_TABLES)
+    out = np.zeros((E, N, K), np.uint16)
+    for t, tab in enumerate(BOUNDARY_TABLES):
+        gmax = float(tab[7])
+        mid = 0.5 * (tab[:-1].astype(np.float64) + tab[1:].astype(np.float64))
+        # the exponent at which 2^e times the smallest nonzero midpoint, rounded down to bf16,
+        # becomes a normal number; the first blocks straddle it, then two blocks whose e clamps
+        lo = mid[mid > 0].min()
+        e_edge = -126 - int(np.floor(np.log2(lo)))
+        fixed = [gmax * 2.0 ** (e_edge + d) * 0.75 for d in range(-2, 3)] + \
+                [3.0e38 * 0.9, gmax * 2.0 ** -140]
+        nblk = 0
+        for n in range(N):
+            for b in range(K // 32):
+                ex = int(g.integers(-150, 130))
+                amax = min(gmax * 2.0 ** ex * g.uniform(0.5, 1.0), 3.0e38)
+                if nblk < len(fixed):
+                    amax = fixed[nblk]
+                elif g.random() < 0.05:
+                    amax = 3.0e38 * g.uniform(0.3, 1.0)
+                nblk += 1
+                v = amax * 2.0 ** (-g.uniform(0, 12, 32)) * np.where(g.random(32) < .5, -1, 1)
+                v[0] = amax
+                v[g.random(32) < 0.05] = 0.0
+                bits = synth.bf16_bits_from_f32(v.astype(np.float32))
+                e = int(oracle.block_scale_bytes(bits[None], gmax)[0, 0]) - 127
+                for j in range(2, 32, 3):
+                    with np.errstate(over="ignore"):        # beyond fp32: skipped below
+                        tie = int(synth.bf16_bits_from_f32(
+                            np.array([mid[g.integers(0, 7)] * 2.0 ** e], np.float32))[0])
+                    step = int(g.integers(-1, 2))
+                    cand = tie + step if 0 < (tie & 0x7FFF) < 0x7F7F else tie
+                    if (cand & 0x7FFF) <= (int(bits[0]) & 0x7FFF):
+                        bits[j] = (cand & 0x7FFF) | (0x8000 if g.random() < .5 else 0)
+                out[t, n, b * 32:(b + 1) * 32] = bits
+    return out
+
+
+def test_quantize_exponent_and_threshold_boundaries():
+    """The scale byte and the nearest magnitude against the oracle, bit for bit, across block
+    exponents on both sides of every range limit the kernel's integer decision has (thresholds
+    leaving the normal range, exponents clamped at +-127) and on exact ties."""
+    mq = _mq()
+    N, K = 24, 256
+    bits = _boundary_weights(57, N, K)
+    for group in ((0, 1, 2, 3), (4, 5)):               # at most 4 tables per call
+        tabs = BOUNDARY_TABLES[list(group)]
+        gb = np.ascontiguousarray(bits[list(group)])
+        E = len(group)
+        tid = np.arange(E, dtype=np.uint8)
+        codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device="cuda")
+        err = torch.empty(E * N, dtype=torch.float64, device="cuda")
+        mq.moeq_quantize(dev(gb.view(np.int16)), E, N, K, tabs, dev(tid), codes, scales, err)
+        gc, gs, ge = host(codes), host(scales), host(err).reshape(E, N)
+        err2 = torch.empty_like(err)
+        mq.moeq_quantize(dev(gb.view(np.int16)), E, N, K, tabs, dev(tid), None, None, err2)
+        np.testing.assert_array_equal(host(err2).view(np.uint64), host(err).view(np.uint64))
+        for i, t in enumerate(group):
+            tab = BOUNDARY_TABLES[t]
+            rc, rs = oracle.rtn_encode(gb[i], tab)
+            np.testing.assert_array_equal(gs[i], rs, err_msg=f"table {t}")
+            np.testing.assert_array_equal(gc[i], rc, err_msg=f"table {t}")
+            re = oracle.reconstruction_sq_error(gb[i], rc, rs, tab)
+            np.testing.assert_allclose(ge[i], re, rtol=1e-12, atol=1e-300, err_msg=f"table {t}")
+
+
 def test_quantize_invalid_table_id_gives_nan_blocks():
     mq = _mq()
     E, N, K = 2, 8, 96
