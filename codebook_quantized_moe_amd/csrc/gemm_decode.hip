@@ -161,6 +161,19 @@ __device__ inline int active_tiles(const MetaLoads& ml, ExpertMeta& m) {
     return m.n;
 }
 
+// Sum over the 16 K-slices of an MFMA result, i.e. over lanes q, q + 4, ..., q + 60 for each
+// q: within each row of 16 lanes by DPP rotations by 4 and 8 (fused into the adds), then the
+// two row pairs and the two halves by the permlane swaps (the sum of both outputs of a swap is
+// each lane's value plus its partner's). Every lane ends with its q's total; no LDS.
+__device__ __forceinline__ float kslice_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 struct Item {
     int e, cb, r0, rows, tsel;
 };
@@ -429,18 +442,14 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
             buf ^= 1;
         }
 
-        // ---- item complete: sum the 16 K-slices (lanes q, q + 4, ..., q + 60) ----
+        // ---- item complete: sum the 16 K-slices (lanes q, q + 4, ..., q + 60) of the
+        // item's rows (the others are never written) ----
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int r = 0; r < 4; ++r) {
+            if (r >= cur.rows) continue;          // uniform per wavefront
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float v = acc[g][r];
-                v += __shfl_xor(v, 4, 64);
-                v += __shfl_xor(v, 8, 64);
-                v += __shfl_xor(v, 16, 64);
-                v += __shfl_xor(v, 32, 64);
-                acc[g][r] = v;
-            }
+            for (int g = 0; g < 4; ++g) acc[g][r] = kslice_sum(acc[g][r]);
+        }
         if (lane < 4) {
             // lane q holds rows 0..3 of this wavefront's columns 4 g + q
             if (GATEUP) {
