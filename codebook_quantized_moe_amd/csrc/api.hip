@@ -250,13 +250,17 @@ static int projection(const char* w, bool gateup, const uint16_t* act, int T, in
     a.queue = static_cast<int32_t*>(ws);
     const long touched = (long)(E < T * k ? E : T * k);
     clear_hip_error();
-    if (gateup) {
-        // both projection families read x in the decoder's pair-split K order
+    const bool prefill = use_prefill_path(T, k, E);
+    if (gateup && prefill) {
+        // the many-rows kernels read x in the decoder's pair-split K order
         uint16_t* xs = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + prefill_queue_bytes());
         launch_pair_split_rows(static_cast<const uint16_t*>(act), T, H, xs, cu_count(), stream);
         a.act = xs;
+    } else if (gateup) {
+        // the few-rows kernels reorder the x rows they stage, in LDS
+        a.act_natural = 1;
     }
-    if (use_prefill_path(T, k, E)) {
+    if (prefill) {
         // upper bound of the 128-row tiles the device will find
         const long tiles = touched + (long)T * k / prefill_tile_rows();
         const char* groups_env = getenv("MOEQ_PREFILL_WORKGROUPS");   // testing only

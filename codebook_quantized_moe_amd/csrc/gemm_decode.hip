@@ -301,8 +301,8 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
     // start of the chunk before and waited for at its end:
     //   * activations: kTileRows rows x kARowUnits 16-byte units (the last unit of a row is
     //     padding, so that the 4 rows of an MFMA operand read sit in different banks);
-    //     the rows are already in pair-split K order (x is split once per call, the
-    //     intermediate is stored that way);
+    //     the intermediate is stored in pair-split K order; x (natural order) is put into it
+    //     by the wavefront that staged it (split_own below), or comes split (single launch);
     //   * scales: row R of the item (gate|up: R = 64 mat + channel, so gate rows and up rows
     //     fill separate DMA loads) gets kSRow bytes from the 16-byte boundary at or below its
     //     first scale byte of the chunk; readers add the row's offset (row * K/32 mod 16, zero
@@ -360,6 +360,26 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
         }
     };
 
+    // x in natural K order (gate|up from moeq_gateup_swiglu): each wavefront puts the
+    // activation units its own staging loads wrote into pair-split order once they have landed
+    // (its vmcnt wait), before the barrier that publishes the buffer to the other wavefronts.
+    // The same units (and no others) as stage_dma's activation loads of this wavefront.
+    const bool natural = GATEUP && a.act_natural != 0;
+    auto split_own = [&](const Src& sr, int sbufi) {
+        if constexpr (!GATEUP) return;
+        if (!natural || sr.rows <= 0) return;
+        const int na =
+            min(kALoads, ((sr.rows - 1) * kARowUnits + kChunkK / 8 + 63) / 64);
+        uint8_t* ab = abuf + sbufi * kABufBytes;
+        for (int i = wave; i < na; i += S::kWaves) {
+            const int u = i * 64 + lane;
+            if (u < kAUnits) {
+                u32x4* pu = reinterpret_cast<u32x4*>(ab + (size_t)u * 16);
+                *pu = pair_split(*pu);
+            }
+        }
+    };
+
     // ---------------- main loop ----------------
     // Per chunk of kSteps K-steps: the next chunk (of this item or the next one) is staged by
     // DMA into the other buffers; the codes of K-step s sit in one of two register slots (cA
@@ -378,6 +398,8 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
     load_step(cur, 0, cA);
     load_step(cur, 1, cB);         // an item has at least kSteps >= 2 K-steps
     MOEQ_DEC_WAIT_VMCNT(8);        // the staging has landed; the 8 code loads may be in flight
+    asm volatile("" ::: "memory");
+    split_own(cur, 0);
     __syncthreads();
     int buf = 0;
 
@@ -438,6 +460,8 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
                         nx ? j + 2 - kSteps : st + 2);
             }
             MOEQ_DEC_WAIT_VMCNT(4 * kSteps);
+            asm volatile("" ::: "memory");
+            split_own(ns, buf ^ 1);
             __syncthreads();
             buf ^= 1;
         }

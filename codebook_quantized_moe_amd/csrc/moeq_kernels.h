@@ -25,6 +25,8 @@ struct SkinnyArgs {
     int K;                        // contraction length: H (gate|up) or I (down)
     int out_ld;                   // row stride of out, in elements
     int32_t* queue;               // prefill: 8 work-queue counters (device, zeroed per launch)
+    int act_natural;              // few-rows gate|up: act is x in natural K order, put into
+                                  // pair-split order in LDS after staging (else already split)
     TableArgs tables;
 };
 
