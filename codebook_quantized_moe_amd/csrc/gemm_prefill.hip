@@ -520,37 +520,78 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
         asm volatile("" : "+v"(el));              // computed here, not kept live across the loop
         const int hr = 4 * (el >> 5), ecl = el & 31;
         if (GATEUP) {
+            // Each 32-row block of the wavefront's 32 channels goes through LDS (64 bytes a row
+            // in pair-split slot order, in the wavefront's own 2 KB of activation tile 0; see the
+            // down epilogue below), so that a lane stores 16 contiguous bytes (8 slots) instead
+            // of 2.
+            uint16_t* own = reinterpret_cast<uint16_t*>(atile + wave * 2048);
             const int ch = cb * 256 + wave * 32 + ecl;
-            const int slotc = (ch & ~7) | (((ch & 1) << 2) | ((ch & 7) >> 1));
-            uint16_t* ob = reinterpret_cast<uint16_t*>(a.out) + (size_t)(r0 + hr) * a.out_ld + slotc;
+            const int sl = (ecl & ~7) | (((ecl & 1) << 2) | ((ecl & 7) >> 1));  // slot in the 32
+            int rd = lane;
+            asm volatile("" : "+v"(rd));                 // computed here, not kept live across the loop
+            const int gslot = cb * 256 + wave * 32 + 8 * (rd & 3);
+            uint16_t* ob = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
                 if (i >= mt_act) continue;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int c = i * 32 + 8 * (r >> 2) + (r & 3);
-                    if (hr >= rows - c || ch >= N) continue;
+                    const int c = hr + 8 * (r >> 2) + (r & 3);
                     const float v =
                         badtab ? __builtin_nanf("") : silu_mul(acc[i][0][r], acc[i][1][r]);
-                    ob[(size_t)c * a.out_ld] = (uint16_t)f32_to_bf16_rne(v);
+                    own[c * 32 + sl] = (uint16_t)f32_to_bf16_rne(v);
                 }
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int rb = (rd >> 2) + 16 * k;        // row of the block
+                    const int row = 32 * i + rb;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(own + rb * 32 + 8 * (rd & 3));
+                    if (row < rows && gslot < N)
+                        *reinterpret_cast<u32x4*>(ob + (size_t)(r0 + row) * a.out_ld + gslot) = v;
+                }
+                __builtin_amdgcn_wave_barrier();
             }
+            (void)ch;
+            MOEQ_WAIT_LGKM0();
         } else {
-            const int col = cb * 512 + wave * 64 + ecl;
-            float* ob = reinterpret_cast<float*>(a.out) + (size_t)(r0 + hr) * a.out_ld + col;
+            // Each 32-row block of the wavefront's 64 columns goes through LDS, so that a lane
+            // stores 16 contiguous bytes (16 lanes one 256-byte output row, 4 rows a store)
+            // instead of 4: the block (32 rows x 256 bytes) sits in the wavefront's own part of
+            // the four activation tiles (bytes 2048 w .. + 2047 of each, which only this
+            // wavefront's staging loads fill), 8 rows a tile. After run()'s barrier no other
+            // wavefront reads them, and the LDS reads are waited for before this wavefront's
+            // next staging loads.
+            uint8_t* own = atile + wave * 2048;
+            auto blk = [&](int row, int col) { return own + (row >> 3) * kPATile + (row & 7) * 256 + col * 4; };
+            int rd = lane;
+            asm volatile("" : "+v"(rd));                 // computed here, not kept live across the loop
+            const int rl = rd >> 4, c4 = (rd & 15) * 4;   // read side: rows rl + 4 k, 4 columns
+            const int gcol = cb * 512 + wave * 64 + c4;
+            float* ob = reinterpret_cast<float*>(a.out);
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
                 if (i >= mt_act) continue;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int c = i * 32 + 8 * (r >> 2) + (r & 3);
-                    if (hr >= rows - c) continue;
-                    const float wgt = badtab ? __builtin_nanf("") : s_roww[hr + c];
+                    const int c = hr + 8 * (r >> 2) + (r & 3);
 #pragma unroll
                     for (int j = 0; j < NT; ++j)
-                        if (col + 32 * j < N) ob[(size_t)c * a.out_ld + 32 * j] = wgt * acc[i][j][r];
+                        *reinterpret_cast<float*>(blk(c, ecl + 32 * j)) = acc[i][j][r];
                 }
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int row = 32 * i + rl + 4 * k;      // row of the item
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(blk(rl + 4 * k, c4));
+                    if (row < rows && gcol < N) {
+                        const float wgt = badtab ? __builtin_nanf("") : s_roww[row];
+                        *reinterpret_cast<f32x4*>(ob + (size_t)(r0 + row) * a.out_ld + gcol) = wgt * v;
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();
             }
+            MOEQ_WAIT_LGKM0();
         }
         claim = __builtin_amdgcn_readfirstlane(s_claim);
     }
