@@ -90,12 +90,17 @@ __device__ __forceinline__ f32x4 mfma4x4x4(uint32_t a0, uint32_t a1, uint32_t b0
 // table id and the prefix count of its kTileRows-row tiles. Everything the K loop needs about
 // an item then comes from LDS: a vector-memory load inside the loop would have to wait for
 // every code load issued before it (loads return in order) and drain the prefetch.
+// The tiles of the few-rows kernels: at most 4096 rows (every expert adds at most one partial
+// tile of 4): 1024 + 256.
+constexpr int kMaxTiles = 1280;
+
 struct ExpertMeta {
     int active[256];
     int tpre[257];
     int beg[256];
     int cnt[256];
     int tsel[256];
+    uint16_t t2a[kMaxTiles];        // tile -> index of its active expert (when MAP)
     int n;
 };
 
@@ -120,8 +125,9 @@ __device__ __forceinline__ MetaLoads load_meta(const int32_t* offsets, const uin
     return l;
 }
 
-// Fills m from the first wavefront's loads ml (all threads call it; ends with a barrier).
-// Returns the count of active experts.
+// Fills m from the first wavefront's loads ml (all threads call it; ends with a barrier), and
+// with MAP the tile -> expert map. Returns the count of active experts.
+template <bool MAP>
 __device__ inline int active_tiles(const MetaLoads& ml, ExpertMeta& m) {
     const int lane = threadIdx.x & 63;
     if (threadIdx.x < 64) {
@@ -158,6 +164,14 @@ __device__ inline int active_tiles(const MetaLoads& ml, ExpertMeta& m) {
         }
     }
     __syncthreads();
+    if constexpr (MAP) {
+        const int nact = m.n;
+        for (int a = threadIdx.x; a < nact; a += blockDim.x) {
+            const int t1 = min(m.tpre[a + 1], kMaxTiles);
+            for (int t = m.tpre[a]; t < t1; ++t) m.t2a[t] = (uint16_t)a;
+        }
+        __syncthreads();
+    }
     return m.n;
 }
 
@@ -178,18 +192,27 @@ struct Item {
     int e, cb, r0, rows, tsel;
 };
 
+template <bool MAP>
 __device__ __forceinline__ Item locate(long item, int ncb, int nact, const ExpertMeta& m) {
     Item it;
-    const int tile = (int)(item / ncb);
-    it.cb = (int)(item % ncb);
-    // last a < nact with tpre[a] <= tile: a fixed, unrolled search (no loop in the K loop)
-    int lo = 0;
+    int lo = 0, tile;
+    if constexpr (MAP) {
+        // one LDS read: the map of active_tiles<true> (items < 2^31)
+        const int idx = (int)item;
+        tile = idx / ncb;
+        it.cb = idx - tile * ncb;
+        lo = __builtin_amdgcn_readfirstlane((int)m.t2a[tile]);
+    } else {
+        tile = (int)(item / ncb);
+        it.cb = (int)(item % ncb);
+        // last a < nact with tpre[a] <= tile: a fixed, unrolled search (no loop in the K loop)
 #pragma unroll
-    for (int step = 128; step >= 1; step >>= 1) {
-        const int c = lo + step;
-        if (c < nact && m.tpre[c] <= tile) lo = c;
+        for (int step = 128; step >= 1; step >>= 1) {
+            const int c = lo + step;
+            if (c < nact && m.tpre[c] <= tile) lo = c;
+        }
+        lo = __builtin_amdgcn_readfirstlane(lo);
     }
-    lo = __builtin_amdgcn_readfirstlane(lo);
     it.e = __builtin_amdgcn_readfirstlane(m.active[lo]);
     const int m0 = (tile - __builtin_amdgcn_readfirstlane(m.tpre[lo])) * kTileRows;
     it.r0 = __builtin_amdgcn_readfirstlane(m.beg[lo]) + m0;
@@ -237,7 +260,7 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
         if (GATEUP) row_tok[r] = (uint16_t)(p / a.k);
         else row_w[r] = a.topk_w[p];
     }
-    const int nact = active_tiles(ml, meta);
+    const int nact = active_tiles<SALIGN && !GATEUP>(ml, meta);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -268,7 +291,7 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
     auto make_src = [&](long item) {
         Src sr;
         const bool valid = item < items;
-        const Item it = locate(valid ? item : first, ncb, nact, meta);
+        const Item it = locate<SALIGN && !GATEUP>(valid ? item : first, ncb, nact, meta);
         sr.e = it.e;
         sr.cb = it.cb;
         sr.r0 = it.r0;
