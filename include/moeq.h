@@ -83,8 +83,10 @@ const char* moeq_last_error(void);
 /* Bytes of device workspace that moeq_gateup_swiglu and moeq_down need for these sizes
  * (0 means they accept ws = NULL). Currently 256 + T * H * 2 rounded up to 256: the first
  * 256 bytes hold the work-queue counters of the many-rows kernels (the call clears them on
- * its stream before use), the rest a copy of x that gate|up writes with every 8-element
- * group in the pair-split order of moeq_inter_slot. The workspace must be 16-byte aligned;
+ * its stream before use), the rest a copy of x that gate|up writes, when it takes the
+ * many-rows kernels, with every 8-element group in the pair-split order of moeq_inter_slot
+ * (the few-rows kernels reorder the rows they stage, in LDS). The workspace must be 16-byte
+ * aligned;
  * its contents are scratch between calls (two calls that run at the same time need two
  * workspaces). */
 size_t moeq_workspace_bytes(int T, int k, int E, int H, int I);
@@ -190,7 +192,8 @@ int moeq_gateup_swiglu(const uint16_t* x, int T, int H, int I, int E, int k,
  * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation): moeq_gateup_swiglu without the workspace
  * arguments. Its scratch (moeq_workspace_bytes(T, k, E, H, I) bytes: the work-queue counters
- * and the pair-split copy of x) lives in a static device array of this library,
+ * and the pair-split copy of x of the many-rows kernels) lives in a static device array of
+ * this library,
  * MOEQ_STATIC_SCRATCH_BYTES long, which every GPU the library runs on holds until the process
  * ends. The call allocates nothing; its first call on a device looks that array's address up
  * on the device. Arguments, kernels and results are those of moeq_gateup_swiglu.
