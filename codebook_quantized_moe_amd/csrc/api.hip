@@ -433,7 +433,7 @@ int moeq_shared_expert(const uint16_t* x, int T, int H, int I, const uint8_t* ga
 
 // Workspace of moeq_moe_decode, in 256-byte aligned regions.
 struct DecodeWs {
-    size_t bar, ids, w, offsets, sorted_pair, pair_pos, xs, inter, yp, total;
+    size_t bar, ids, w, offsets, sorted_pair, pair_pos, inter, yp, total;
 };
 
 static size_t up256(size_t n) { return (n + 255) / 256 * 256; }
@@ -448,7 +448,6 @@ static DecodeWs decode_ws(int T, int k, int E, int H, int I) {
     d.offsets = o;      o += up256((size_t)(E + 1) * 4);
     d.sorted_pair = o;  o += up256(P * 4);
     d.pair_pos = o;     o += up256(P * 4);
-    d.xs = o;           o += up256((size_t)T * H * 2);
     d.inter = o;        o += up256(P * I * 2);
     d.yp = o;           o += up256(P * H * 4);
     d.total = o;
@@ -577,7 +576,6 @@ int moeq_moe_decode(const uint16_t* x, const float* logits, int T, int H, int I,
     L.offsets = reinterpret_cast<int32_t*>(b + d.offsets);
     L.sorted_pair = reinterpret_cast<int32_t*>(b + d.sorted_pair);
     L.pair_pos = reinterpret_cast<int32_t*>(b + d.pair_pos);
-    uint16_t* xs = reinterpret_cast<uint16_t*>(b + d.xs);
     uint16_t* inter = reinterpret_cast<uint16_t*>(b + d.inter);
     float* yp = reinterpret_cast<float*>(b + d.yp);
     // both projections validated as the per-step calls would (their workspace is unused here)
@@ -599,7 +597,8 @@ int moeq_moe_decode(const uint16_t* x, const float* logits, int T, int H, int I,
         a.k = k;
         a.E = E;
         if (gateup) {
-            a.act = xs;
+            a.act = x;                    // natural order, split in LDS
+            a.act_natural = 1;
             a.act_bytes = (uint32_t)((long long)T * H * 2);
             a.codes0 = gate_codes; a.scales0 = gate_scales;
             a.codes1 = up_codes; a.scales1 = up_scales;
@@ -619,9 +618,6 @@ int moeq_moe_decode(const uint16_t* x, const float* logits, int T, int H, int I,
     if (int r = fill(L.dn, false)) return r;
     L.logits = logits;
     L.sigmoid = gating == MOEQ_GATING_SIGMOID_TOPK ? 1 : 0;
-    L.x = reinterpret_cast<const u32x4*>(x);
-    L.xs = reinterpret_cast<u32x4*>(xs);
-    L.x_units = (long)T * H / 8;
     L.yp = yp;
     L.residual = residual;
     L.y = y;

@@ -232,12 +232,23 @@ __device__ __forceinline__ int weight_row(int cb, int w, int g, int q, int* mat)
     return cb * S::kRowsPerWG + w * 16 + g * 4 + q;
 }
 
+// An output element: a plain store, or (COH) a device-coherent one, which goes through the
+// XCD's L2 to memory, so that workgroups on the other XCDs can read it in the same launch.
+template <bool COH, class T>
+__device__ __forceinline__ void put(T* p, T v) {
+    if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+
 // One projection over the whole persistent grid (every workgroup calls it; it returns when
 // the workgroup's items are done). smem: the launch's dynamic LDS; meta: LDS for the item map.
 // SALIGN (only when every weight row's scale bytes start on a 16-byte boundary, K/32 a
 // multiple of 16) stages 16 fewer scale bytes per row; the other form works for any K.
-template <bool GATEUP, class S, bool SALIGN>
-__device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, ExpertMeta& meta) {
+// COH: outputs by device-coherent stores (single launch). build: fill the decode tables
+// (false when the launch has already filled them for these tables).
+template <bool GATEUP, class S, bool SALIGN, bool COH = false>
+__device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, ExpertMeta& meta,
+                                            bool build = true) {
     constexpr int kChunkK = S::kChunkK, kRowsPerWG = S::kRowsPerWG;
     constexpr int kARowUnits = S::kARowUnits, kABufBytes = S::kABufBytes;
     constexpr int kSBufBytes = S::kSBufBytes, kSRowBytes = S::kSRowBytes;
@@ -254,7 +265,7 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
     const int p0 = has_row ? a.sorted_pair[threadIdx.x] : 0;
     MetaLoads ml;
     if (threadIdx.x < 64) ml = load_meta(a.offsets, a.table_id, a.E);
-    build_decode_tables(a.tables, tab);
+    if (build) build_decode_tables(a.tables, tab);
     for (int r = threadIdx.x; r < P; r += blockDim.x) {
         const int p = r == (int)threadIdx.x ? p0 : a.sorted_pair[r];
         if (GATEUP) row_tok[r] = (uint16_t)(p / a.k);
@@ -511,7 +522,8 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
                         if (r >= cur.rows) continue;
                         const float v = badtab ? __builtin_nanf("")
                                                : silu_mul(acc[h][r], acc[2 + h][r]);
-                        out[(size_t)(cur.r0 + r) * a.out_ld + slot] = (uint16_t)f32_to_bf16_rne(v);
+                        put<COH>(out + (size_t)(cur.r0 + r) * a.out_ld + slot,
+                                 (uint16_t)f32_to_bf16_rne(v));
                     }
                 }
             } else {
@@ -525,7 +537,8 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
                     for (int g = 0; g < 4; ++g) {
                         const int col = cur.cb * kRowsPerWG + wave * 16 + g * 4 + q;
                         if (col >= N) continue;
-                        out[row * a.out_ld + col] = badtab ? __builtin_nanf("") : wgt * acc[g][r];
+                        put<COH>(out + row * a.out_ld + col,
+                                 badtab ? __builtin_nanf("") : wgt * acc[g][r]);
                     }
                 }
             }
@@ -582,33 +595,51 @@ void launch_decode(const SkinnyArgs& a, bool gateup, long tiles, int cus, int sh
 }
 
 // ---------------------------------------------------------------------------------------------
-// The whole decode layer in one cooperative launch: routing and permutation (workgroup 0) beside
-// the pair-split copy of x (the other workgroups), gate|up, down, combine, with a grid barrier
-// between phases. The grid is co-resident (a cooperative launch fails rather than run it
-// otherwise). A barrier gives up after about a second of waiting and records that in the
-// barrier word, so a broken barrier ends the kernel instead of hanging it.
+// The whole decode layer in one cooperative launch: routing and permutation (workgroup 0, while
+// the others fill their decode tables), gate|up, down and the combine over the whole grid. The
+// grid is co-resident (a cooperative launch fails rather than run it otherwise).
+//
+// Coherence across the 8 XCDs (each has its own L2) without cache maintenance in the grid
+// barriers: every value that one phase writes and a later phase reads on another XCD is written
+// with device-coherent stores (the projections' outputs) and, at the time it is read, was never
+// read in this launch before, so no L2 or L1 holds a stale copy of its line (the launch starts
+// with clean caches, and every 128-byte line of the intermediate and of the expert outputs has
+// one writing workgroup). A barrier then only needs each thread's stores to have completed
+// before its workgroup arrives. The routing arrays are written with plain stores by workgroup 0
+// alone, which writes its XCD's L2 back once before it raises the ready flag.
+// Waits give up after about a second and record that in the barrier header, so a broken
+// barrier ends the kernel instead of hanging it.
+//
+// Barrier header (ints): 0 arrivals, 1 failure flag, 2..11 the clock stamps, 12 routing ready.
 // ---------------------------------------------------------------------------------------------
 constexpr int kBarrierSpinLimit = 1 << 22;
+constexpr int kBarReady = 12;
 
-__device__ inline void grid_barrier(int* bar, int target) {
-    __syncthreads();
+// thread 0 waits until *p >= target (bounded); the whole workgroup then continues
+__device__ inline void wait_at_least(int* bar, int* p, int target) {
     if (threadIdx.x == 0) {
-        __threadfence();                          // this workgroup's writes before its arrival
-        __hip_atomic_fetch_add(&bar[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         int spins = 0;
-        while (__hip_atomic_load(&bar[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(8);
+        while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(2);
             if (++spins > kBarrierSpinLimit) {
                 __hip_atomic_fetch_or(&bar[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
         }
-        __threadfence();                          // the others' writes after the wait
     }
     __syncthreads();
 }
 
-template <class S>
+// all workgroups: this workgroup's (device-coherent) stores are complete, then it arrives
+__device__ inline void grid_barrier(int* bar, int target) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(&bar[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_at_least(bar, &bar[0], target);
+}
+
+template <class S, bool SALIGN>
 __global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 decode_layer_kernel(const DecodeLayerArgs L) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -628,20 +659,24 @@ decode_layer_kernel(const DecodeLayerArgs L) {
             route_token(L.logits, t, L.E, L.k, L.sigmoid != 0, L.ids, L.w);
         __syncthreads();
         permute_block<S::kWaves>(L.ids, P, L.E, L.offsets, L.sorted_pair, L.pair_pos);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");    // L2 write-back of this XCD
+            __builtin_amdgcn_s_waitcnt(0);                        // ... completed
+            __hip_atomic_store(&L.barrier[kBarReady], 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
-    if (blockIdx.x > 0 || nwg == 1) {
-        const long first = nwg == 1 ? tid : (long)(blockIdx.x - 1) * S::kThreads + tid;
-        const long step = (long)(nwg == 1 ? 1 : nwg - 1) * S::kThreads;
-        for (long i = first; i < L.x_units; i += step)
-            L.xs[i] = pair_split(__builtin_nontemporal_load(L.x + i));
-    }
-    grid_barrier(L.barrier, nwg);
+    // the decode tables (the same for both projections) while workgroup 0 routes
+    build_decode_tables(L.gu.tables, reinterpret_cast<u32x4*>(smem));
+    wait_at_least(L.barrier, &L.barrier[kBarReady], 1);
     stamp(1);
-    decode_body<true, S, false>(L.gu, smem, meta);
-    grid_barrier(L.barrier, 2 * nwg);
+    decode_body<true, S, SALIGN, true>(L.gu, smem, meta, false);
+    grid_barrier(L.barrier, nwg);
     stamp(2);
-    decode_body<false, S, false>(L.dn, smem, meta);
-    grid_barrier(L.barrier, 3 * nwg);
+    decode_body<false, S, SALIGN, true>(L.dn, smem, meta, false);
+    grid_barrier(L.barrier, 2 * nwg);
     stamp(3);
     // phase 4: combine, 4 columns per thread
     const int quads = L.H / 4;
@@ -655,7 +690,7 @@ decode_layer_kernel(const DecodeLayerArgs L) {
 }
 
 __global__ void zero_barrier_kernel(int* bar) {
-    if (threadIdx.x < 2) bar[threadIdx.x] = 0;
+    if (threadIdx.x < 16) bar[threadIdx.x] = 0;
 }
 
 // Launch geometry of the fused kernel: dynamic LDS and the largest co-resident grid.
@@ -665,22 +700,28 @@ static size_t decode_layer_lds(const DecodeLayerArgs& L) {
            (size_t)L.T * L.k * 4;
 }
 
-int launch_decode_layer(const DecodeLayerArgs& L, int cus, hipStream_t stream) {
+template <bool SALIGN>
+static int launch_layer(const DecodeLayerArgs& L, int cus, hipStream_t stream) {
     using S = DecShape<8, 2048>;
     const size_t lds = decode_layer_lds(L);
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_layer_kernel<S>, S::kThreads,
-                                                     lds) != hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_layer_kernel<S, SALIGN>,
+                                                     S::kThreads, lds) != hipSuccess || per_cu < 1)
         return -1;
     const int blocks = cus * per_cu;
     hipLaunchKernelGGL(zero_barrier_kernel, dim3(1), dim3(64), 0, stream, L.barrier);
     DecodeLayerArgs arg = L;
     void* params[] = {&arg};
-    if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(decode_layer_kernel<S>),
+    if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(decode_layer_kernel<S, SALIGN>),
                                    dim3(blocks), dim3(S::kThreads), params, (unsigned)lds,
                                    stream) != hipSuccess)
         return -2;
     return blocks;
+}
+
+int launch_decode_layer(const DecodeLayerArgs& L, int cus, hipStream_t stream) {
+    return scale_rows_aligned(L.gu) && scale_rows_aligned(L.dn) ? launch_layer<true>(L, cus, stream)
+                                                                : launch_layer<false>(L, cus, stream);
 }
 
 }  // namespace moeq

@@ -58,9 +58,6 @@ struct DecodeLayerArgs {
     SkinnyArgs gu, dn;            // the two projections (routing arrays inside the workspace)
     const float* logits;          // [T, E]
     int sigmoid;                  // gating: 0 softmax, 1 sigmoid
-    const u32x4* x;               // [T, H] bf16 as 16-byte units
-    u32x4* xs;                    // its pair-split copy
-    long x_units;                 // T * H / 8
     int32_t* ids;                 // [T*k]
     float* w;                     // [T*k]
     int32_t* offsets;             // [E + 1]
@@ -69,7 +66,7 @@ struct DecodeLayerArgs {
     const float* yp;              // [T*k, H] (the down projection's output)
     const uint16_t* residual;     // [T, H] or null
     uint16_t* y;                  // [T, H]
-    int* barrier;                 // 2 ints: arrivals, failure flag
+    int* barrier;                 // header: arrivals, failure flag, clock stamps, ready flag
     int T, k, E, H;
 };
 // returns the grid size, or < 0 when the cooperative launch was refused

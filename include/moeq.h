@@ -293,12 +293,13 @@ int moeq_unpermute_combine_shared(const float* yp, const int32_t* pair_pos,
  * same results, run as phases of one grid separated by grid barriers (README of
  * GLM-5.2-EXL3-TR3v4-3.5bpw-MTP78, "Tuning" / "Why": one fused launch per layer, a grid the
  * size of the machine; cutting launches gained decode throughput). Workgroup 0 routes and
- * permutes while the others write the pair-split copy of x; then gate|up, down and the
- * combine run on the whole grid.
+ * permutes while the others fill their decode tables; then gate|up, down and the combine run
+ * on the whole grid. The projections' outputs are written with device-coherent stores, so the
+ * barriers between the phases need no cache write-back or invalidation.
  *   x, logits, weights, tables, table_id, gating: as for the per-step calls
  *   residual bf16 [T, H] or NULL; y bf16 [T, H] out (may be the residual buffer)
  *   ws       moeq_moe_decode_workspace_bytes(T, k, E, H, I) bytes, 256-byte aligned: the
- *            barrier words, routing arrays, pair-split x, intermediate and expert outputs
+ *            barrier words, routing arrays, intermediate and expert outputs
  *            (scratch between calls; calls that overlap need their own). Bytes 8..47 receive
  *            five 64-bit stamps of the device's constant 100 MHz clock, taken by workgroup 0
  *            at the start and after each of the four phases (for profiling).
