@@ -242,8 +242,9 @@ __device__ __forceinline__ void put(T* p, T v) {
 
 // One projection over the whole persistent grid (every workgroup calls it; it returns when
 // the workgroup's items are done). smem: the launch's dynamic LDS; meta: LDS for the item map.
-// SALIGN (only when every weight row's scale bytes start on a 16-byte boundary, K/32 a
-// multiple of 16) stages 16 fewer scale bytes per row; the other form works for any K.
+// SALIGN (only when K is a multiple of the chunk, so every K-step lies inside K and every
+// weight row's scale bytes start on a 16-byte boundary) stages 16 fewer scale bytes per row
+// and checks no K bounds; the other form works for any K.
 // COH: outputs by device-coherent stores (single launch). build: fill the decode tables
 // (false when the launch has already filled them for these tables).
 template <bool GATEUP, class S, bool SALIGN, bool COH = false>
@@ -321,6 +322,9 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
     // codes of K-step st: lane (b, q) of group g reads 32 codes of row 4 g + q at K 32 b
     auto load_group = [&](const Src& sr, int st, int g) {
         const int kk = st * kStepK;
+        // SALIGN (whole chunks): every step is inside K, and a row past N (kOutOfRange) stays
+        // past the end of the buffer after adding kk / 2 < 2^30
+        if constexpr (SALIGN) return bload16<kStreamPolicy>((GATEUP && g >= 2) ? sr.c1 : sr.c0, sr.off[g] + kk / 2);
         const bool ok = kk + b * 32 < K;
         const uint32_t off = (ok && sr.off[g] != kOutOfRange) ? sr.off[g] + kk / 2 : kOutOfRange;
         return bload16<kStreamPolicy>((GATEUP && g >= 2) ? sr.c1 : sr.c0, off);
@@ -460,7 +464,7 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
 #pragma unroll
             for (int j = 0; j < 4; ++j) A[j] = *reinterpret_cast<const u32x4*>(ap + 16 * j);
             const uint8_t* sp = sbuf + buf * kSBufBytes + (kk % kChunkK) / 32 + b;
-            const bool kin = kk + 32 * b < K;
+            const bool kin = SALIGN || kk + 32 * b < K;
             // the four scale bytes, then their four table entries: two LDS round trips per
             // K-step instead of two per group
             uint32_t sc[4];
@@ -557,7 +561,9 @@ decode_kernel(const SkinnyArgs a) {
 }
 
 // scale rows of K/32 bytes all start on a 16-byte boundary
-static bool scale_rows_aligned(const SkinnyArgs& a) { return (a.K / 32) % 16 == 0; }
+// whole chunks of K (which also puts every scale row on a 16-byte boundary)
+template <class S>
+static bool whole_chunks(const SkinnyArgs& a) { return a.K % S::kChunkK == 0; }
 
 template <class S>
 static void launch_shape(const SkinnyArgs& a, bool gateup, long items, int cus, hipStream_t stream) {
@@ -565,7 +571,7 @@ static void launch_shape(const SkinnyArgs& a, bool gateup, long items, int cus, 
                        (size_t)a.T * a.k * (gateup ? 2 : 4);
     const int per_cu = 16 / S::kWaves;                    // 4 wavefronts per SIMD
     const long blocks = std::max(1L, std::min(items, (long)cus * per_cu));
-    const bool al = scale_rows_aligned(a);
+    const bool al = whole_chunks<S>(a);
     if (gateup && al)
         hipLaunchKernelGGL((decode_kernel<true, S, true>), dim3(blocks), dim3(S::kThreads), lds,
                            stream, a);
@@ -720,7 +726,8 @@ static int launch_layer(const DecodeLayerArgs& L, int cus, hipStream_t stream) {
 }
 
 int launch_decode_layer(const DecodeLayerArgs& L, int cus, hipStream_t stream) {
-    return scale_rows_aligned(L.gu) && scale_rows_aligned(L.dn) ? launch_layer<true>(L, cus, stream)
+    using S = DecShape<8, 2048>;
+    return whole_chunks<S>(L.gu) && whole_chunks<S>(L.dn) ? launch_layer<true>(L, cus, stream)
                                                                 : launch_layer<false>(L, cus, stream);
 }
 
