@@ -371,6 +371,10 @@ def test_layer_empty_batch(path):
 
 @pytest.mark.parametrize("T,E,H,I,k", [(37, 8, 576, 320, 4),     # >16 rows per expert, K tails
                                        (37, 16, 1024, 512, 4),    # 16-byte aligned scale rows
+                                       # down over whole 2048-wide K chunks (no K bound checks)
+                                       # with a last 128-row block half past H; gate|up K tail
+                                       (37, 8, 2112, 2048, 4),
+                                       (5, 4, 4096, 2048, 2),     # whole chunks in both
                                        (1, 16, 256, 128, 16),     # k = E, one token
                                        (64, 4, 256, 192, 4)])     # k = E, 64 rows per expert
 def test_layer_ragged_shapes(T, E, H, I, k, path):
