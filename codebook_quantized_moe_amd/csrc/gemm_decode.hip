@@ -175,18 +175,25 @@ __device__ inline int active_tiles(const MetaLoads& ml, ExpertMeta& m) {
     return m.n;
 }
 
-// Sum over the 16 K-slices of an MFMA result, i.e. over lanes q, q + 4, ..., q + 60 for each
-// q: within each row of 16 lanes by DPP rotations by 4 and 8 (fused into the adds), then the
-// two row pairs and the two halves by the permlane swaps (the sum of both outputs of a swap is
-// each lane's value plus its partner's). Every lane ends with its q's total; no LDS.
-__device__ __forceinline__ float kslice_sum(float v) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
-    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(s[0]) + __uint_as_float(s[1]);
-    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+// Sums over the 16 K-slices of an MFMA result (lane bits 2..5 of lane 4 b + q).
+// split_bit5(x, y): lanes with bit 5 clear get x summed over bit 5, the others y (the sum of
+// the two outputs of v_permlane32_swap); split_bit4 likewise over bit 4 with v_permlane16_swap.
+__device__ __forceinline__ float split_bit5(float x, float y) {
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
     return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
+__device__ __forceinline__ float split_bit4(float x, float y) {
+    const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+// every lane gets the sum over lane bits 2 and 3 (DPP row rotations by 4 and 8, fused into
+// the adds)
+__device__ __forceinline__ float sum_bits23(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+    return v;
+}
+__device__ __forceinline__ float sum_bits234(float v) { return sum_bits23(split_bit4(v, v)); }
 
 struct Item {
     int e, cb, r0, rows, tsel;
@@ -504,46 +511,42 @@ __device__ __forceinline__ void decode_body(const SkinnyArgs& a, uint8_t* smem, 
             buf ^= 1;
         }
 
-        // ---- item complete: sum the 16 K-slices (lanes q, q + 4, ..., q + 60) of the
-        // item's rows (the others are never written) ----
+        // ---- item complete: sum the 16 K-slices (lane bits 2..5) of the item's rows (the
+        // others are never written). The permlane swaps split the sums of two values between
+        // the two halves of the lane bit they exchange, so each lane ends with the totals it
+        // stores: gate|up, bit 5 picks h and the lane keeps gate and up of channel 4 h + q;
+        // down, bits 5 and 4 pick the column group g. The other bits are summed by DPP. ----
+        if (GATEUP) {
+            uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+            const int h = lane >> 5;
+            const int ch = cur.cb * S::kChannelsPerWG + wave * 8 + h * 4 + q;
+            const int slot = (ch & ~7) | (((ch & 1) << 2) | ((ch & 7) >> 1));
+            const bool st = (lane & 0x1C) == 0 && ch < N;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if (r >= cur.rows) continue;          // uniform per wavefront
-#pragma unroll
-            for (int g = 0; g < 4; ++g) acc[g][r] = kslice_sum(acc[g][r]);
-        }
-        if (lane < 4) {
-            // lane q holds rows 0..3 of this wavefront's columns 4 g + q
-            if (GATEUP) {
-                uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int ch = cur.cb * S::kChannelsPerWG + wave * 8 + h * 4 + q;
-                    if (ch >= N) continue;
-                    const int slot = (ch & ~7) | (((ch & 1) << 2) | ((ch & 7) >> 1));
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if (r >= cur.rows) continue;
-                        const float v = badtab ? __builtin_nanf("")
-                                               : silu_mul(acc[h][r], acc[2 + h][r]);
-                        put<COH>(out + (size_t)(cur.r0 + r) * a.out_ld + slot,
-                                 (uint16_t)f32_to_bf16_rne(v));
-                    }
+            for (int r = 0; r < 4; ++r) {
+                if (r >= cur.rows) continue;          // uniform per wavefront
+                const float gv = sum_bits234(split_bit5(acc[0][r], acc[1][r]));
+                const float uv = sum_bits234(split_bit5(acc[2][r], acc[3][r]));
+                if (st) {
+                    const float v = badtab ? __builtin_nanf("") : silu_mul(gv, uv);
+                    put<COH>(out + (size_t)(cur.r0 + r) * a.out_ld + slot,
+                             (uint16_t)f32_to_bf16_rne(v));
                 }
-            } else {
-                float* out = reinterpret_cast<float*>(a.out);
+            }
+        } else {
+            float* out = reinterpret_cast<float*>(a.out);
+            const int g = ((lane >> 5) << 1) | ((lane >> 4) & 1);
+            const int col = cur.cb * kRowsPerWG + wave * 16 + g * 4 + q;
+            const bool st = (lane & 0x0C) == 0 && col < N;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (r >= cur.rows) continue;
+            for (int r = 0; r < 4; ++r) {
+                if (r >= cur.rows) continue;          // uniform per wavefront
+                const float v = sum_bits23(split_bit4(split_bit5(acc[0][r], acc[2][r]),
+                                                      split_bit5(acc[1][r], acc[3][r])));
+                if (st) {
                     const size_t row = (size_t)(cur.r0 + r);
-                    const float wgt = row_w[row];
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int col = cur.cb * kRowsPerWG + wave * 16 + g * 4 + q;
-                        if (col >= N) continue;
-                        put<COH>(out + row * a.out_ld + col,
-                                 badtab ? __builtin_nanf("") : wgt * acc[g][r]);
-                    }
+                    put<COH>(out + row * a.out_ld + col,
+                             badtab ? __builtin_nanf("") : row_w[row] * v);
                 }
             }
         }
