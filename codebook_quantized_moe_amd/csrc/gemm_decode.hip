@@ -3,9 +3,9 @@
 // MFMA shape. v_mfma_f32_4x4x4_16b_bf16 runs 16 independent 4x4x4 products; lane 4b + q holds
 // row q of block b's A (4 K values), column q of block b's B, and column q (rows 0..3) of
 // block b's result. The 16 blocks are used as 16 slices of K of one 4-row x 4-column product
-// and summed by a lane butterfly when an item is complete. A tile therefore has M = 4 token
-// rows (the size of an expert's share of a decode batch) instead of a 16-row operand that
-// would be mostly padding.
+// and summed across lanes (permlane swaps, DPP rotations) when an item is complete. A tile
+// therefore has M = 4 token rows (the size of an expert's share of a decode batch) instead of
+// a 16-row operand that would be mostly padding.
 //
 // Memory path. On MI355X the vector-memory address path, not HBM, bounds a weight stream that
 // is fetched with narrow or out-of-range loads: a wavefront instruction costs about the same
