@@ -64,8 +64,11 @@ def expert_bytes(H, I):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # a decode step is ~0.25 ms, and the first steps after a synchronize run slower than the
+    # steady state (8-token layer, GPU time per step over 20 / 100 / 400 back-to-back steps:
+    # 245 / 223 / 217 us), so the defaults time enough steps for the steady state to dominate
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=None, choices=[1, 2, 3, 4, 5],
                     help="measure this workload alone (default: the decode headline plus the "
                          "other four in the configs block)")
